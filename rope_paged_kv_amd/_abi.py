@@ -1,0 +1,86 @@
+"""ctypes declarations of the C ABI in include/rpkv.h (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+RPKV_OK, RPKV_EINVAL, RPKV_EHIP, RPKV_ENOSPACE, RPKV_ESTATE = 0, -1, -2, -3, -4
+RPKV_BF16, RPKV_F32 = 0, 1
+RPKV_MAX_POOL_PAGES = 512
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librpkv.so")
+
+EXPORTS = ("rope3d_tables_bytes", "rope3d_build_tables", "kv_required_bytes", "kv_create",
+           "kv_destroy", "kv_reset", "kv_append_frame", "attend_frame", "kv_evict_deferred",
+           "kv_read_state", "kv_get_info", "rpkv_strerror")
+
+
+class Rope3dSpec(C.Structure):
+    _fields_ = [("head_dim", C.c_int), ("pairs_t", C.c_int), ("pairs_h", C.c_int),
+                ("pairs_w", C.c_int), ("theta", C.c_double), ("ntk_factor", C.c_double),
+                ("max_frames", C.c_int), ("max_h", C.c_int), ("max_w", C.c_int)]
+
+
+class KvConfig(C.Structure):
+    _fields_ = [("num_layers", C.c_int), ("num_streams", C.c_int), ("num_heads", C.c_int),
+                ("head_dim", C.c_int), ("dtype", C.c_int), ("grid_h", C.c_int),
+                ("grid_w", C.c_int), ("special_tokens", C.c_int), ("patch_page_size", C.c_int),
+                ("special_page_size", C.c_int), ("scale_frames", C.c_int),
+                ("sliding_window", C.c_int), ("max_keyframes", C.c_int), ("attn_splits", C.c_int),
+                ("rope", Rope3dSpec)]
+
+
+_P = RPKV_MAX_POOL_PAGES
+
+
+class KvStateHost(C.Structure):
+    _fields_ = [("status", C.c_int), ("fresh", C.c_int), ("n_free", C.c_int), ("n_scale", C.c_int),
+                ("n_window", C.c_int), ("n_special_tokens", C.c_int), ("target_page", C.c_int),
+                ("special_offset", C.c_int), ("n_visible_pages", C.c_int),
+                ("visible_special_pages", C.c_int), ("last_page_len", C.c_int),
+                ("visible_special_tokens", C.c_int), ("free_list", C.c_int * _P),
+                ("scale_pages", C.c_int * _P), ("window_pages", C.c_int * _P),
+                ("visible_pages", C.c_int * _P)]
+
+
+class KvInfo(C.Structure):
+    _fields_ = [("num_layers", C.c_int), ("num_streams", C.c_int), ("num_heads", C.c_int),
+                ("head_dim", C.c_int), ("dtype", C.c_int), ("tokens_per_frame", C.c_int),
+                ("pool_pages", C.c_int), ("slot_capacity", C.c_int), ("special_capacity", C.c_int),
+                ("attn_splits", C.c_int), ("page_bytes", C.c_size_t), ("cache_bytes", C.c_size_t),
+                ("total_bytes", C.c_size_t), ("off_kpool", C.c_size_t), ("off_vpool", C.c_size_t),
+                ("off_ksp", C.c_size_t), ("off_vsp", C.c_size_t), ("frames_appended", C.c_longlong),
+                ("frames_committed", C.c_longlong)]
+
+
+_lib = None
+
+
+def load() -> C.CDLL:
+    """Loads librpkv.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m rope_paged_kv_amd.build`")
+    lib = C.CDLL(LIB_PATH)
+    vp, i, sz = C.c_void_p, C.c_int, C.c_size_t
+    sig = {
+        "rope3d_tables_bytes": (sz, [C.POINTER(Rope3dSpec)]),
+        "rope3d_build_tables": (i, [C.POINTER(Rope3dSpec), vp, sz, vp]),
+        "kv_required_bytes": (sz, [C.POINTER(KvConfig)]),
+        "kv_create": (i, [C.POINTER(KvConfig), vp, sz, vp, C.POINTER(vp)]),
+        "kv_destroy": (i, [vp]),
+        "kv_reset": (i, [vp, i, vp]),
+        "kv_append_frame": (i, [vp, i, i, i, vp, vp, vp, vp, vp, vp]),
+        "attend_frame": (i, [vp, i, vp, vp, vp, vp]),
+        "kv_evict_deferred": (i, [vp, i, vp]),
+        "kv_read_state": (i, [vp, i, i, C.POINTER(KvStateHost), vp]),
+        "kv_get_info": (i, [vp, C.POINTER(KvInfo)]),
+        "rpkv_strerror": (C.c_char_p, [i]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    _lib = lib
+    return lib

@@ -1,0 +1,258 @@
+// Fused 3D rotary embedding + paged KV append + bookkeeping commit.
+//
+// What is computed (page "How 3D RoPE Positional Encoding Works with the
+// Paged KV Cache in LingBot-Map": "Complex-Valued Tensor Application",
+// "Frame Appending and Position Encoding Integration", "Dual-Stream Memory
+// Layout", "Attention Computation with Cached RoPE"; page "KV Caching Benefits
+// in Ling Bot-Map": "Reduced KV Growth via Keyframe Streaming"):
+//  * every (x[2j], x[2j+1]) pair of Q and K is rotated by the angle of its
+//    token's (t, h, w) position on the pair's axis -- a complex product done
+//    in real fp32 arithmetic, rounded once to the storage dtype;
+//  * rotated K and raw V of the patch tokens go to the frame's patch page,
+//    those of the special tokens to the special stream; rotated Q goes to
+//    q_rot for the attention kernel;
+//  * the target page is the free-list top, else the next never-used page; a
+//    keyframe commits it (scale list first, then the window) and its special
+//    tokens, a skip-append frame only writes the tentative slot;
+//  * the visible page table is rebuilt: scale pages, window pages oldest
+//    first, the frame's own page if it is tentative, then the special pages
+//    and the last special page's length.
+//
+// Layout of the work: one workgroup per (tile of 64 tokens, head, stream);
+// tile 0 carries the special tokens.  Each thread moves 16-byte chunks, so
+// every row (one token of one head, 128 B in bf16) is read and written with
+// full-width coalesced accesses; V goes through LDS to be written transposed
+// (the layout the attention kernel's matrix-core operands read).  The
+// bookkeeping never leaves the device: every workgroup derives the target page
+// from the state as it stands, and the last workgroup to arrive (atomic
+// ticket) commits the new state.
+#include "rpkv_internal.h"
+
+namespace rpkv {
+
+template <typename T>
+struct Vec;
+
+template <>
+struct Vec<uint16_t> {   // bf16 bit patterns
+    static constexpr int kCh = 8;
+    __device__ static inline void unpack(const uint4& r, float* f) {
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
+    __device__ static inline uint32_t pack2(float lo, float hi) {
+        // round to nearest even (inputs are finite)
+        uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+        a += 0x7FFFu + ((a >> 16) & 1u);
+        b += 0x7FFFu + ((b >> 16) & 1u);
+        return (a >> 16) | (b & 0xFFFF0000u);
+    }
+    __device__ static inline uint4 pack(const float* f) {
+        return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+    }
+};
+
+template <>
+struct Vec<float> {
+    static constexpr int kCh = 4;
+    __device__ static inline void unpack(const uint4& r, float* f) {
+        f[0] = __uint_as_float(r.x);
+        f[1] = __uint_as_float(r.y);
+        f[2] = __uint_as_float(r.z);
+        f[3] = __uint_as_float(r.w);
+    }
+    __device__ static inline uint4 pack(const float* f) {
+        return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                          __float_as_uint(f[3]));
+    }
+};
+
+// Rotates the kCh/2 pairs of one chunk of Q and of K: pair j uses the t table
+// for j < pt, the h table for the next ph pairs and the w table after that.
+template <int kPairs>
+__device__ inline void rotate_pairs(float* fq, float* fk, int j0, const AppendArgs& a, int hp,
+                                    int wp) {
+#pragma unroll
+    for (int p = 0; p < kPairs; ++p) {
+        const int j = j0 + p;
+        float2 cs;
+        if (j < a.pt)
+            cs = a.tab_t[a.frame * a.pt + j];
+        else if (j < a.pt + a.ph)
+            cs = a.tab_h[hp * a.ph + (j - a.pt)];
+        else
+            cs = a.tab_w[wp * a.pw + (j - a.pt - a.ph)];
+        const float xq = fq[2 * p], yq = fq[2 * p + 1];
+        fq[2 * p] = xq * cs.x - yq * cs.y;
+        fq[2 * p + 1] = xq * cs.y + yq * cs.x;
+        const float xk = fk[2 * p], yk = fk[2 * p + 1];
+        fk[2 * p] = xk * cs.x - yk * cs.y;
+        fk[2 * p + 1] = xk * cs.y + yk * cs.x;
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
+    constexpr int CH = Vec<T>::kCh;        // elements per 16-byte chunk
+    constexpr int CPR = kHeadDim / CH;     // chunks per row
+    constexpr int NCH = kTile * CPR;       // chunks per tile and tensor
+    constexpr int PER = NCH / 256;         // chunks per thread
+    __shared__ T vt[kTile][kHeadDim + CH];
+    __shared__ int s_last;
+
+    const int tile = blockIdx.x, h = blockIdx.y, s = blockIdx.z, tid = threadIdx.x;
+    CacheState* st = a.states + s;
+
+    // Target of this append, from the state as it stands.
+    const int status = st->status;
+    const int n_free = st->n_free;
+    const int fresh = st->fresh;
+    const int page = n_free > 0 ? st->free_[n_free - 1] : fresh;
+    const int sp_off = st->n_sp;
+    const bool ok = status == RPKV_OK && (n_free > 0 || fresh < a.pool) &&
+                    (!a.commit || sp_off + a.nsp <= a.max_kf * a.nsp);
+
+    const bool special = tile == 0;
+    const int slot0 = special ? 0 : (tile - 1) * kTile;
+    const int nrows = special ? a.nsp : min(kTile, a.P - slot0);
+    const int tok0 = special ? 0 : a.nsp + slot0;
+
+    const size_t rs = (size_t)a.H * kHeadDim;  // elements between consecutive tokens
+    const size_t in_off = ((size_t)s * a.N + tok0) * rs + (size_t)h * kHeadDim;
+    const T* qb = (const T*)a.q + in_off;
+    const T* kb = (const T*)a.k + in_off;
+    const T* vb = (const T*)a.v + in_off;
+    T* qrb = (T*)a.q_rot + in_off;
+    T* kdst;
+    if (special)
+        kdst = (T*)a.ksp + s * a.ksp_elems + ((size_t)h * a.sp_cap + sp_off) * kHeadDim;
+    else
+        kdst = (T*)a.kpool + s * a.kpool_elems +
+               (((size_t)h * a.pool + page) * a.slot_cap + slot0) * kHeadDim;
+
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int id = tid + i * 256;
+        const int r = id / CPR, c = id % CPR;
+        const bool valid = r < nrows;
+        uint4 qv = make_uint4(0, 0, 0, 0), kv = qv, vv = qv;
+        if (valid) {
+            qv = *(const uint4*)(qb + r * rs + c * CH);
+            kv = *(const uint4*)(kb + r * rs + c * CH);
+            vv = *(const uint4*)(vb + r * rs + c * CH);
+        }
+        int hp = 0, wp = 0;   // specials and rows past the tile sit at h = w = 0
+        if (!special && valid) {
+            const int p = slot0 + r;
+            hp = p / a.gw;
+            wp = p - hp * a.gw;
+        }
+        float fq[CH], fk[CH];
+        Vec<T>::unpack(qv, fq);
+        Vec<T>::unpack(kv, fk);
+        rotate_pairs<CH / 2>(fq, fk, c * (CH / 2), a, hp, wp);
+        if (valid) {
+            *(uint4*)(qrb + r * rs + c * CH) = Vec<T>::pack(fq);
+            if (ok) *(uint4*)(kdst + r * kHeadDim + c * CH) = Vec<T>::pack(fk);
+        }
+        *(uint4*)&vt[r][c * CH] = vv;   // zeros for rows past the tile's tokens
+    }
+    __syncthreads();
+
+    if (ok) {
+        if (!special) {
+            // V^T rows d of the page, storage positions slot0 .. slot0+63.
+            T* vdst = (T*)a.vpool + s * a.kpool_elems +
+                      ((size_t)h * a.pool + page) * kHeadDim * a.slot_cap + slot0;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int id = tid + i * 256;
+                const int d = id / CPR, g = id % CPR;
+                union {
+                    T t[CH];
+                    uint4 u;
+                } pk;
+#pragma unroll
+                for (int e = 0; e < CH; ++e) pk.t[e] = vt[vslot_perm(g * CH + e)][d];
+                *(uint4*)(vdst + (size_t)d * a.slot_cap + g * CH) = pk.u;
+            }
+        } else {
+            T* vdst = (T*)a.vsp + s * a.ksp_elems + (size_t)h * kHeadDim * a.sp_cap;
+            for (int id = tid; id < a.nsp * kHeadDim; id += 256) {
+                const int r = id / kHeadDim, d = id % kHeadDim;
+                vdst[(size_t)d * a.sp_cap + vslot_perm(sp_off + r)] = vt[r][d];
+            }
+        }
+    }
+
+    // Arrival: the last workgroup of this stream commits the bookkeeping.
+    __syncthreads();
+    if (tid == 0) {
+        __threadfence();
+        const int t = atomicAdd(&st->ticket, 1);
+        s_last = (t == a.n_tiles * a.H - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+
+    // Visible patch pages: old scale pages, old window oldest first, then the
+    // frame's page (committed to the scale list or the window, or tentative:
+    // in every case it comes last).
+    const int ns = st->n_scale, nw = st->n_win, head = st->win_head;
+    const int vis_n = ok ? ns + nw + 1 : 0;
+    for (int i = tid; i < vis_n; i += 256)
+        st->vis[i] = i < ns ? st->scale[i] : (i < ns + nw ? st->win[(head + i - ns) % kMaxPool] : page);
+    __syncthreads();
+    if (tid == 0) {
+        if (!ok) {
+            st->status = status != RPKV_OK ? status : RPKV_ENOSPACE;
+            st->vis_n = 0;
+            st->vis_sp_tokens = 0;
+            st->vis_sp_pages = 0;
+            st->last_page_len = 0;
+        } else {
+            int vis_sp;
+            if (a.commit) {
+                if (n_free > 0)
+                    st->n_free = n_free - 1;
+                else
+                    st->fresh = fresh + 1;
+                if (ns < a.sf) {
+                    st->scale[ns] = page;
+                    st->n_scale = ns + 1;
+                } else {
+                    st->win[(head + nw) % kMaxPool] = page;
+                    st->n_win = nw + 1;
+                }
+                st->n_sp = sp_off + a.nsp;
+                vis_sp = sp_off + a.nsp;
+            } else {
+                vis_sp = sp_off + a.nsp;
+            }
+            const int sp_pages = (vis_sp + a.sp_page - 1) / a.sp_page;
+            st->target = page;
+            st->sp_off = sp_off;
+            st->vis_n = vis_n;
+            st->vis_sp_tokens = vis_sp;
+            st->vis_sp_pages = sp_pages;
+            st->last_page_len = sp_pages ? vis_sp - (sp_pages - 1) * a.sp_page : 0;
+        }
+        st->ticket = 0;
+    }
+}
+
+hipError_t launch_rope_append(const AppendArgs& a, int dtype, hipStream_t st) {
+    dim3 grid(a.n_tiles, a.H, a.S);
+    if (dtype == RPKV_BF16)
+        hipLaunchKernelGGL(k_rope_append<uint16_t>, grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_rope_append<float>, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace rpkv

@@ -1,0 +1,353 @@
+// Host side of the C ABI declared in include/rpkv.h: argument checks, the
+// device-memory layout of a handle, rotary-table construction and kernel
+// launches.  No call synchronises the host except rope3d_build_tables (its
+// copy) and kv_read_state.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "rpkv_internal.h"
+
+using namespace rpkv;
+
+struct kv_handle {
+    kv_config cfg;
+    Layout L;
+    char* base;
+    size_t bytes;
+    long long appended, committed;
+};
+
+namespace {
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool spec_ok(const rope3d_spec* r) {
+    return r && r->head_dim > 0 && r->head_dim % 2 == 0 && r->pairs_t >= 0 && r->pairs_h >= 0 &&
+           r->pairs_w >= 0 && r->pairs_t + r->pairs_h + r->pairs_w == r->head_dim / 2 &&
+           r->theta > 0 && r->ntk_factor > 0 && r->max_frames >= 1 && r->max_h >= 1 && r->max_w >= 1;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Picks the number of key-range splits of the bf16 attention: enough
+// workgroups to fill the chip about once (256 CUs x 4 resident workgroups),
+// without splits shorter than 8 key tiles at full cache occupancy.
+int auto_splits(const Layout& L) {
+    const int base = L.q_tiles * L.H * L.S;
+    const int max_tiles = L.pool * L.tpp + (L.sp_cap + kTile - 1) / kTile;
+    int s = (1024 + base / 2) / base;
+    s = s < max_tiles / 8 ? s : max_tiles / 8;
+    s = s > 32 ? 32 : s;
+    return s < 1 ? 1 : s;
+}
+
+bool layout(const kv_config* c, Layout* L) {
+    if (!c) return false;
+    if (c->num_layers < 1 || c->num_streams < 1 || c->num_heads < 1 || c->head_dim != kHeadDim)
+        return false;
+    if (c->dtype != RPKV_BF16 && c->dtype != RPKV_F32) return false;
+    if (c->grid_h < 1 || c->grid_w < 1 || c->special_tokens < 0 || c->special_tokens > kTile)
+        return false;
+    const long long P = (long long)c->grid_h * c->grid_w;
+    if (P > (1 << 20) || c->patch_page_size < P || c->special_page_size < 1) return false;
+    if (c->scale_frames < 0 || c->sliding_window < 0 ||
+        c->scale_frames + c->sliding_window + 1 > kMaxPool)
+        return false;
+    if (c->max_keyframes < 0 || c->attn_splits < 0) return false;
+    if (!spec_ok(&c->rope) || c->rope.head_dim != c->head_dim || c->rope.max_h < c->grid_h ||
+        c->rope.max_w < c->grid_w)
+        return false;
+    Layout& l = *L;
+    l.S = c->num_streams;
+    l.H = c->num_heads;
+    l.P = (int)P;
+    l.nsp = c->special_tokens;
+    l.N = l.nsp + l.P;
+    l.gh = c->grid_h;
+    l.gw = c->grid_w;
+    l.pool = c->scale_frames + c->sliding_window + 1;
+    l.slot_cap = (int)round_up((size_t)c->patch_page_size, kTile);
+    l.sp_page = c->special_page_size;
+    // committed specials + one tentative frame, whole special pages, 64-aligned
+    const size_t sp_tok = (size_t)(c->max_keyframes + 1) * c->special_tokens;
+    const size_t sp_pages_tok = round_up(sp_tok, (size_t)c->special_page_size);
+    l.sp_cap = (int)round_up(sp_pages_tok > 0 ? sp_pages_tok : 1, kTile);
+    l.sf = c->scale_frames;
+    l.W = c->sliding_window;
+    l.max_kf = c->max_keyframes;
+    l.tpp = (l.P + kTile - 1) / kTile;
+    l.q_tiles = (l.N + 127) / 128;
+    l.elem = c->dtype == RPKV_BF16 ? 2 : 4;
+    if (c->dtype == RPKV_F32)
+        l.splits = 1;
+    else
+        l.splits = c->attn_splits > 0 ? (c->attn_splits > 64 ? 64 : c->attn_splits) : auto_splits(l);
+    l.state_bytes = round_up(sizeof(CacheState), 256);
+    l.kpool_elems = (size_t)l.H * l.pool * l.slot_cap * kHeadDim;
+    l.ksp_elems = (size_t)l.H * l.sp_cap * kHeadDim;
+    const size_t caches = (size_t)c->num_layers * l.S;
+    l.off_state = 0;
+    l.off_kpool = round_up(caches * l.state_bytes, 256);
+    l.off_vpool = l.off_kpool + round_up(caches * l.kpool_elems * l.elem, 256);
+    l.off_ksp = l.off_vpool + round_up(caches * l.kpool_elems * l.elem, 256);
+    l.off_vsp = l.off_ksp + round_up(caches * l.ksp_elems * l.elem, 256);
+    l.off_part_o = l.off_vsp + round_up(caches * l.ksp_elems * l.elem, 256);
+    const size_t parts = l.splits > 1 ? (size_t)l.S * l.H * l.splits * l.N : 0;
+    l.off_part_lse = l.off_part_o + round_up(parts * kHeadDim * 4, 256);
+    l.total = l.off_part_lse + round_up(parts * 4, 256);
+    return true;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? RPKV_OK : RPKV_EHIP; }
+
+CacheState* states_of(kv_handle* h, int layer) {
+    return (CacheState*)(h->base + h->L.off_state) + (size_t)layer * h->L.S;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rope3d_tables_bytes(const rope3d_spec* s) {
+    if (!spec_ok(s)) return 0;
+    return ((size_t)s->max_frames * s->pairs_t + (size_t)s->max_h * s->pairs_h +
+            (size_t)s->max_w * s->pairs_w) * 2 * sizeof(float);
+}
+
+// Per-axis tables of (cos, sin)(pos * omega_j), omega_j = (theta*ntk)^(-2j/d_a),
+// d_a = 2*pairs_a, computed in double and rounded once to float.
+int rope3d_build_tables(const rope3d_spec* s, void* d_tables, size_t bytes, void* stream) {
+    const size_t need = rope3d_tables_bytes(s);
+    if (!need || !d_tables || bytes < need) return RPKV_EINVAL;
+    float* host = (float*)malloc(need);
+    if (!host) return RPKV_EINVAL;
+    const double base = s->theta * s->ntk_factor;
+    const int rows[3] = {s->max_frames, s->max_h, s->max_w};
+    const int pairs[3] = {s->pairs_t, s->pairs_h, s->pairs_w};
+    size_t o = 0;
+    for (int ax = 0; ax < 3; ++ax) {
+        const int np = pairs[ax];
+        for (int pos = 0; pos < rows[ax]; ++pos)
+            for (int j = 0; j < np; ++j) {
+                const double omega = pow(base, -2.0 * j / (2.0 * np));
+                const double ang = (double)pos * omega;
+                host[o++] = (float)cos(ang);
+                host[o++] = (float)sin(ang);
+            }
+    }
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(d_tables, host, need, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    free(host);
+    return hip_status(e);
+}
+
+size_t kv_required_bytes(const kv_config* cfg) {
+    Layout L;
+    return layout(cfg, &L) ? L.total : 0;
+}
+
+int kv_create(const kv_config* cfg, void* d_mem, size_t bytes, void* stream, kv_handle** out) {
+    if (!out) return RPKV_EINVAL;
+    *out = nullptr;
+    Layout L;
+    if (!layout(cfg, &L) || !d_mem || ((uintptr_t)d_mem & 255) || bytes < L.total) return RPKV_EINVAL;
+    kv_handle* h = new (std::nothrow) kv_handle;
+    if (!h) return RPKV_EINVAL;
+    h->cfg = *cfg;
+    h->L = L;
+    h->base = (char*)d_mem;
+    h->bytes = bytes;
+    h->appended = h->committed = 0;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = launch_fill_zero(d_mem, L.total, st);
+    if (e == hipSuccess) e = launch_reset(states_of(h, 0), cfg->num_layers * L.S, st);
+    if (e != hipSuccess) {
+        delete h;
+        return RPKV_EHIP;
+    }
+    *out = h;
+    return RPKV_OK;
+}
+
+int kv_destroy(kv_handle* h) {
+    delete h;
+    return RPKV_OK;
+}
+
+int kv_reset(kv_handle* h, int layer, void* stream) {
+    if (!h || layer < -1 || layer >= h->cfg.num_layers) return RPKV_EINVAL;
+    const int first = layer < 0 ? 0 : layer;
+    const int count = (layer < 0 ? h->cfg.num_layers : 1) * h->L.S;
+    if (layer <= 0) h->appended = h->committed = 0;
+    return hip_status(launch_reset(states_of(h, first), count, (hipStream_t)stream));
+}
+
+int kv_append_frame(kv_handle* h, int layer, int frame_idx, int commit, const void* q,
+                    const void* k, const void* v, void* q_rot, const void* d_tables,
+                    void* stream) {
+    if (!h || layer < 0 || layer >= h->cfg.num_layers) return RPKV_EINVAL;
+    if (frame_idx < 0 || frame_idx >= h->cfg.rope.max_frames || (commit != 0 && commit != 1))
+        return RPKV_EINVAL;
+    if (!q || !k || !v || !q_rot || !d_tables) return RPKV_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_rot) || !aligned16(d_tables))
+        return RPKV_EINVAL;
+    const Layout& L = h->L;
+    const rope3d_spec& r = h->cfg.rope;
+    AppendArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.q_rot = q_rot;
+    a.tab_t = (const float2*)d_tables;
+    a.tab_h = a.tab_t + (size_t)r.max_frames * r.pairs_t;
+    a.tab_w = a.tab_h + (size_t)r.max_h * r.pairs_h;
+    a.states = states_of(h, layer);
+    const size_t caches_before = (size_t)layer * L.S;
+    a.kpool = h->base + L.off_kpool + caches_before * L.kpool_elems * L.elem;
+    a.vpool = h->base + L.off_vpool + caches_before * L.kpool_elems * L.elem;
+    a.ksp = h->base + L.off_ksp + caches_before * L.ksp_elems * L.elem;
+    a.vsp = h->base + L.off_vsp + caches_before * L.ksp_elems * L.elem;
+    a.kpool_elems = L.kpool_elems;
+    a.ksp_elems = L.ksp_elems;
+    a.S = L.S;
+    a.N = L.N;
+    a.H = L.H;
+    a.P = L.P;
+    a.gw = L.gw;
+    a.nsp = L.nsp;
+    a.pool = L.pool;
+    a.slot_cap = L.slot_cap;
+    a.sp_cap = L.sp_cap;
+    a.sp_page = L.sp_page;
+    a.sf = L.sf;
+    a.max_kf = L.max_kf;
+    a.pt = r.pairs_t;
+    a.ph = r.pairs_h;
+    a.pw = r.pairs_w;
+    a.frame = frame_idx;
+    a.commit = commit;
+    a.n_tiles = 1 + L.tpp;
+    const int rc = hip_status(launch_rope_append(a, h->cfg.dtype, (hipStream_t)stream));
+    if (rc == RPKV_OK && layer == 0) {
+        h->appended++;
+        h->committed += commit;
+    }
+    return rc;
+}
+
+int attend_frame(kv_handle* h, int layer, const void* q_rot, void* out, float* lse, void* stream) {
+    if (!h || layer < 0 || layer >= h->cfg.num_layers || !q_rot || !out) return RPKV_EINVAL;
+    if (!aligned16(q_rot) || !aligned16(out) || ((uintptr_t)lse & 3)) return RPKV_EINVAL;
+    const Layout& L = h->L;
+    AttnArgs a;
+    a.q = q_rot;
+    a.out = out;
+    a.lse = lse;
+    a.states = states_of(h, layer);
+    const size_t caches_before = (size_t)layer * L.S;
+    a.kpool = h->base + L.off_kpool + caches_before * L.kpool_elems * L.elem;
+    a.vpool = h->base + L.off_vpool + caches_before * L.kpool_elems * L.elem;
+    a.ksp = h->base + L.off_ksp + caches_before * L.ksp_elems * L.elem;
+    a.vsp = h->base + L.off_vsp + caches_before * L.ksp_elems * L.elem;
+    a.kpool_elems = L.kpool_elems;
+    a.ksp_elems = L.ksp_elems;
+    a.part_o = (float*)(h->base + L.off_part_o);
+    a.part_lse = (float*)(h->base + L.off_part_lse);
+    a.S = L.S;
+    a.N = L.N;
+    a.H = L.H;
+    a.P = L.P;
+    a.pool = L.pool;
+    a.slot_cap = L.slot_cap;
+    a.sp_cap = L.sp_cap;
+    a.tpp = L.tpp;
+    a.splits = L.splits;
+    a.q_tiles = L.q_tiles;
+    a.n_logical = L.q_tiles * L.H * L.S * L.splits;
+    a.scale = 1.0f / sqrtf((float)kHeadDim);
+    a.scale_log2 = (float)(1.0 / sqrt((double)kHeadDim) * 1.4426950408889634);
+    return hip_status(launch_attend(a, h->cfg.dtype, (hipStream_t)stream));
+}
+
+int kv_evict_deferred(kv_handle* h, int layer, void* stream) {
+    if (!h || layer < 0 || layer >= h->cfg.num_layers) return RPKV_EINVAL;
+    return hip_status(launch_evict(states_of(h, layer), h->L.S, h->L.W, (hipStream_t)stream));
+}
+
+int kv_read_state(kv_handle* h, int layer, int stream_idx, kv_state_host* out, void* stream) {
+    if (!h || !out || layer < 0 || layer >= h->cfg.num_layers || stream_idx < 0 ||
+        stream_idx >= h->L.S)
+        return RPKV_EINVAL;
+    CacheState* tmp = (CacheState*)malloc(sizeof(CacheState));
+    if (!tmp) return RPKV_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(tmp, states_of(h, layer) + stream_idx, sizeof(CacheState),
+                                  hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+        free(tmp);
+        return RPKV_EHIP;
+    }
+    memset(out, 0, sizeof(*out));
+    out->status = tmp->status;
+    out->fresh = tmp->fresh;
+    out->n_free = tmp->n_free;
+    out->n_scale = tmp->n_scale;
+    out->n_window = tmp->n_win;
+    out->n_special_tokens = tmp->n_sp;
+    out->target_page = tmp->target;
+    out->special_offset = tmp->sp_off;
+    out->n_visible_pages = tmp->vis_n;
+    out->visible_special_pages = tmp->vis_sp_pages;
+    out->last_page_len = tmp->last_page_len;
+    out->visible_special_tokens = tmp->vis_sp_tokens;
+    for (int i = 0; i < tmp->n_free && i < kMaxPool; ++i) out->free_list[i] = tmp->free_[i];
+    for (int i = 0; i < tmp->n_scale && i < kMaxPool; ++i) out->scale_pages[i] = tmp->scale[i];
+    for (int i = 0; i < tmp->n_win && i < kMaxPool; ++i)
+        out->window_pages[i] = tmp->win[(tmp->win_head + i) % kMaxPool];
+    for (int i = 0; i < tmp->vis_n && i < kMaxPool; ++i) out->visible_pages[i] = tmp->vis[i];
+    free(tmp);
+    return RPKV_OK;
+}
+
+int kv_get_info(const kv_handle* h, kv_info* out) {
+    if (!h || !out) return RPKV_EINVAL;
+    const Layout& L = h->L;
+    out->num_layers = h->cfg.num_layers;
+    out->num_streams = L.S;
+    out->num_heads = L.H;
+    out->head_dim = kHeadDim;
+    out->dtype = h->cfg.dtype;
+    out->tokens_per_frame = L.N;
+    out->pool_pages = L.pool;
+    out->slot_capacity = L.slot_cap;
+    out->special_capacity = L.sp_cap;
+    out->attn_splits = L.splits;
+    out->page_bytes = (size_t)2 * L.H * L.slot_cap * kHeadDim * L.elem;
+    out->cache_bytes = (size_t)2 * (L.kpool_elems + L.ksp_elems) * L.elem;
+    out->total_bytes = L.total;
+    out->off_kpool = L.off_kpool;
+    out->off_vpool = L.off_vpool;
+    out->off_ksp = L.off_ksp;
+    out->off_vsp = L.off_vsp;
+    out->frames_appended = h->appended;
+    out->frames_committed = h->committed;
+    return RPKV_OK;
+}
+
+const char* rpkv_strerror(int code) {
+    switch (code) {
+        case RPKV_OK: return "ok";
+        case RPKV_EINVAL: return "invalid argument";
+        case RPKV_EHIP: return "HIP runtime error";
+        case RPKV_ENOSPACE: return "cache pool or special stream exhausted";
+        case RPKV_ESTATE: return "invalid state";
+        default: return "unknown error";
+    }
+}
+
+}  // extern "C"
