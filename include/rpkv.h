@@ -110,11 +110,14 @@ int rope3d_build_tables(const rope3d_spec* spec, void* d_tables, size_t bytes, v
  *  - special stream: append-only, special_tokens tokens per stored frame in
  *    pages of special_page_size tokens, never evicted; capacity
  *    max_keyframes stored frames (+1 frame of tentative tokens).
- * One cache per (layer, stream).  Only keyframes are stored (commit = 1); a
+ * One cache per (layer, stream).  Every appended frame first lands in the
+ * tentative slot (the page the next stored frame takes and the special tokens
+ * right after the stored ones); its own attention sees it there.  The deferred
+ * eviction call then keeps it if it is a keyframe (commit = 1) -- the page
+ * joins the scale list or the window, its specials the special stream -- and a
  * skip-append frame (commit = 0, [KVB] "Reduced KV Growth via Keyframe
- * Streaming") writes its K/V to the tentative slot (the page the next stored
- * frame would take and the special tokens right after the stored ones): its
- * own attention sees them, nothing keeps them.
+ * Streaming") or a rolled-back one is simply not kept ([KVB] "Dynamic Keyframe
+ * Selection": deferred eviction retains the KV, rollback drops it).
  *
  * Device memory (all inside the caller's d_mem, laid out by the library):
  *  - per cache: bookkeeping state (int32) and the visible page table;
@@ -173,11 +176,13 @@ int kv_reset(kv_handle* h, int layer, void* stream);
  *   q, k, v:   inputs [S][N][H][D]; read only
  *   q_rot:     output [S][N][H][D]: rotated Q for attend_frame
  *   d_tables:  rotary tables built with cfg.rope
- * Rotated K and raw V go to the target page and the special stream; the last
- * workgroup then commits the bookkeeping (if commit) and rebuilds the visible
- * page table: scale pages, window pages oldest first, the tentative page for a
- * skip-append frame, then special pages with their last-page length
- * ([ROPE-KV] "Attention Computation with Cached RoPE").
+ * Rotated K and raw V go to the tentative slot; the visible page table is
+ * rebuilt on the device: scale pages, window pages oldest first, the frame's
+ * own page, then the special pages with their last-page length ([ROPE-KV]
+ * "Attention Computation with Cached RoPE").  `commit` is recorded and applied
+ * by kv_evict_deferred.  A second append without kv_evict_deferred or
+ * kv_rollback in between replaces the first (same tentative slot).
+ * No bookkeeping is read back to the host.
  */
 int kv_append_frame(kv_handle* h, int layer, int frame_idx, int commit, const void* q,
                     const void* k, const void* v, void* q_rot, const void* d_tables,
@@ -198,10 +203,20 @@ int kv_append_frame(kv_handle* h, int layer, int frame_idx, int commit, const vo
 int attend_frame(kv_handle* h, int layer, const void* q_rot, void* out, float* lse, void* stream);
 
 /* Deferred eviction for `layer` ([KVB] "Memory-Efficient Sliding Window
- * Management"; [ROPE-KV] "Dual-Stream Memory Layout"): while a cache's window
- * holds more than sliding_window pages, its oldest page goes to the free list.
+ * Management", "Dynamic Keyframe Selection"; [ROPE-KV] "Dual-Stream Memory
+ * Layout"), run after the frame's attention: first keeps the last appended
+ * frame if it was appended with commit = 1 (ENOSPACE, sticky, if the special
+ * stream already holds max_keyframes frames), then, while a cache's window
+ * holds more than sliding_window pages, moves its oldest page to the free list.
  * Policy parameters are the ones given at kv_create. */
 int kv_evict_deferred(kv_handle* h, int layer, void* stream);
+
+/* Drops the last appended frame of every stream of `layer` instead of keeping
+ * it ([KVB] "Dynamic Keyframe Selection": _rollback_last_frame removes the
+ * temporary KV entry).  Lets a caller decide keyframes after attention:
+ * append with commit = 1, attend, then kv_evict_deferred (keep) or
+ * kv_rollback (drop; a following kv_evict_deferred is a no-op). */
+int kv_rollback(kv_handle* h, int layer, void* stream);
 
 /* Bookkeeping of one cache, copied to the host (test and debug hook). */
 typedef struct {
@@ -215,6 +230,7 @@ typedef struct {
     int visible_special_pages;  /* special pages 0 .. visible_special_pages-1 */
     int last_page_len;          /* valid tokens in the last visible special page */
     int visible_special_tokens;
+    int pending_commit;         /* 1: last appended keyframe not yet kept */
     int free_list[RPKV_MAX_POOL_PAGES];    /* bottom .. top */
     int scale_pages[RPKV_MAX_POOL_PAGES];
     int window_pages[RPKV_MAX_POOL_PAGES]; /* oldest first */

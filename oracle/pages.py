@@ -18,11 +18,15 @@ Keyframe Streaming":
   special pages; the number of valid tokens in the last special page is the
   last-page length.
 
+Every appended frame first goes to the *tentative slot* -- the page the next
+stored frame would take and the special tokens right after the stored ones --
+where its own attention sees it; the deferred-eviction call keeps it if it is
+a keyframe, a rollback (or skip-append) drops it (page "KV Caching Benefits in
+Ling Bot-Map", section "Dynamic Keyframe Selection": the deferred eviction
+retains the current KV, the rollback removes the temporary entry).
+
 Readings (the pages are silent): the free list is a stack (last in, first
-out); a non-keyframe (skip-append) writes its K/V to the *tentative slot* --
-the page the next stored frame would take and the special tokens right after
-the stored ones -- which is visible to that frame's own attention and is not
-committed; the frame being processed is listed after the window.  The free
+out); the frame being processed is listed after the window.  The free
 list never holds more than one page in the workloads, so the stack order does
 not change any page id there.
 """
@@ -64,6 +68,7 @@ class PageSim:
     sp_offset: int = 0              # first special token written by the last append
     page_frame: Dict[int, int] = field(default_factory=dict)   # committed page -> frame
     special_frames: List[int] = field(default_factory=list)    # stored frames, append order
+    pending: Optional[tuple] = None         # (frame, page) of an appended keyframe not yet kept
 
     def __post_init__(self):
         if self.pool_pages is None:
@@ -83,17 +88,44 @@ class PageSim:
         return Visible([], pages, last, tokens)
 
     def append(self, frame: int, commit: bool) -> int:
-        """Append one frame (``commit`` False: skip-append). Returns the status."""
+        """Append one frame to the tentative slot (``commit`` False: skip-append).
+
+        The frame sees its own tokens; whether it is kept is decided by the
+        deferred eviction (``evict``), which retains a keyframe, or by
+        ``rollback``, which drops it.  Returns the status."""
         if self.status != OK:
             return self.status
         t = self.next_page()
-        cap = self.special_capacity
-        if t is None or (cap is not None and self.n_sp + self.n_special > cap):
+        if t is None:
             self.status = ENOSPACE
             self.visible = Visible([], 0, 0, 0)
+            self.pending = None
             return self.status
         self.target, self.sp_offset = t, self.n_sp
-        if commit:
+        vis = self._special_visible(self.n_sp + self.n_special)
+        vis.patch_pages = self.scale + list(self.window) + [t]
+        self.visible = vis
+        self.pending = (frame, t) if commit else None
+        return OK
+
+    def rollback(self):
+        """Drop the last appended frame (it is not kept)."""
+        self.pending = None
+
+    def evict(self) -> List[int]:
+        """Deferred eviction: keep the pending keyframe, then move the oldest
+        window pages to the free list while the window holds more than
+        ``sliding_window``.  Returns the pages freed."""
+        out = []
+        if self.status != OK:
+            return out
+        if self.pending is not None:
+            frame, t = self.pending
+            self.pending = None
+            cap = self.special_capacity
+            if cap is not None and self.n_sp + self.n_special > cap:
+                self.status = ENOSPACE
+                return out
             if self.free:
                 self.free.pop()
             else:
@@ -105,19 +137,6 @@ class PageSim:
             self.page_frame[t] = frame
             self.special_frames.append(frame)
             self.n_sp += self.n_special
-            vis = self._special_visible(self.n_sp)
-            vis.patch_pages = self.scale + list(self.window)
-        else:
-            vis = self._special_visible(self.n_sp + self.n_special)
-            vis.patch_pages = self.scale + list(self.window) + [t]
-        self.visible = vis
-        return OK
-
-    def evict(self) -> List[int]:
-        """Deferred eviction; returns the pages moved to the free list."""
-        out = []
-        if self.status != OK:
-            return out
         while len(self.window) > self.sliding_window:
             p = self.window.popleft()
             self.page_frame.pop(p, None)
@@ -130,6 +149,7 @@ class PageSim:
         self.free, self.scale, self.window = [], [], collections.deque()
         self.visible, self.target, self.sp_offset = None, -1, 0
         self.page_frame, self.special_frames = {}, []
+        self.pending = None
 
     def visible_patch_frames(self, frame: int) -> List[int]:
         """Frames whose patches the current visible table shows (``frame`` for

@@ -80,10 +80,14 @@ def kv_evict_deferred(h, layer: int, stream: int) -> None:
     _check(_lib.kv_evict_deferred(h, layer, stream), "kv_evict_deferred")
 
 
+def kv_rollback(h, layer: int, stream: int) -> None:
+    _check(_lib.kv_rollback(h, layer, stream), "kv_rollback")
+
+
 def kv_read_state(h, layer: int, stream_idx: int, stream: int) -> dict:
     st = _abi.KvStateHost()
     _check(_lib.kv_read_state(h, layer, stream_idx, C.byref(st), stream), "kv_read_state")
-    out = {name: getattr(st, name) for name, _ in _abi.KvStateHost._fields_[:12]}
+    out = {name: getattr(st, name) for name, _ in _abi.KvStateHost._fields_[:13]}
     out["free_list"] = list(st.free_list[:st.n_free])
     out["scale_pages"] = list(st.scale_pages[:st.n_scale])
     out["window_pages"] = list(st.window_pages[:st.n_window])
@@ -165,6 +169,9 @@ class PagedKVCache:
 
     def evict(self, layer):
         kv_evict_deferred(self.h, layer, self.stream)
+
+    def rollback(self, layer):
+        kv_rollback(self.h, layer, self.stream)
 
     def state(self, layer=0, stream_idx=0) -> dict:
         return kv_read_state(self.h, layer, stream_idx, self.stream)

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librpkv.so"
 
 EXPORTS = ("rope3d_tables_bytes", "rope3d_build_tables", "kv_required_bytes", "kv_create",
            "kv_destroy", "kv_reset", "kv_append_frame", "attend_frame", "kv_evict_deferred",
-           "kv_read_state", "kv_get_info", "rpkv_strerror")
+           "kv_rollback", "kv_read_state", "kv_get_info", "rpkv_strerror")
 
 
 class Rope3dSpec(C.Structure):
@@ -38,7 +38,8 @@ class KvStateHost(C.Structure):
                 ("n_window", C.c_int), ("n_special_tokens", C.c_int), ("target_page", C.c_int),
                 ("special_offset", C.c_int), ("n_visible_pages", C.c_int),
                 ("visible_special_pages", C.c_int), ("last_page_len", C.c_int),
-                ("visible_special_tokens", C.c_int), ("free_list", C.c_int * _P),
+                ("visible_special_tokens", C.c_int), ("pending_commit", C.c_int),
+                ("free_list", C.c_int * _P),
                 ("scale_pages", C.c_int * _P), ("window_pages", C.c_int * _P),
                 ("visible_pages", C.c_int * _P)]
 
@@ -75,6 +76,7 @@ def load() -> C.CDLL:
         "kv_append_frame": (i, [vp, i, i, i, vp, vp, vp, vp, vp, vp]),
         "attend_frame": (i, [vp, i, vp, vp, vp, vp]),
         "kv_evict_deferred": (i, [vp, i, vp]),
+        "kv_rollback": (i, [vp, i, vp]),
         "kv_read_state": (i, [vp, i, i, C.POINTER(KvStateHost), vp]),
         "kv_get_info": (i, [vp, C.POINTER(KvInfo)]),
         "rpkv_strerror": (C.c_char_p, [i]),

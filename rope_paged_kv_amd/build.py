@@ -1,6 +1,7 @@
 """Builds librpkv.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-    python -m rope_paged_kv_amd.build
+    python rope_paged_kv_amd/build.py      (run by path: importing the package
+                                            loads the library this builds)
 """
 from __future__ import annotations
 

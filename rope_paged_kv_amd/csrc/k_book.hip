@@ -1,11 +1,14 @@
-// Cache bookkeeping kernels: zero fill, reset and deferred eviction.
+// Cache bookkeeping kernels: zero fill, reset, commit + deferred eviction,
+// rollback.
 //
-// Deferred eviction follows "KV Caching Benefits in Ling Bot-Map", section
+// Deferred eviction follows "KV Caching Benefits in Ling Bot-Map", sections
 // "Memory-Efficient Sliding Window Management" (eviction runs once the frame
-// has been processed) and "How 3D RoPE Positional Encoding Works with the
-// Paged KV Cache in LingBot-Map", section "Dual-Stream Memory Layout" (the
-// oldest window page goes back to the free list; scale pages and the special
-// stream are never evicted).
+// has been processed) and "Dynamic Keyframe Selection" (the deferred-eviction
+// call is what retains a keyframe's KV; a rollback drops the temporary entry),
+// and "How 3D RoPE Positional Encoding Works with the Paged KV Cache in
+// LingBot-Map", section "Dual-Stream Memory Layout" (the oldest window page
+// goes back to the free list; scale pages and the special stream are never
+// evicted).
 #include "rpkv_internal.h"
 
 namespace rpkv {
@@ -23,7 +26,7 @@ __global__ void k_reset(CacheState* states, int count) {
     int c = blockIdx.x;
     if (c >= count || threadIdx.x != 0) return;
     CacheState* s = states + c;
-    s->ticket = 0;
+    s->pending = 0;
     s->status = RPKV_OK;
     s->fresh = 0;
     s->n_free = 0;
@@ -39,13 +42,41 @@ __global__ void k_reset(CacheState* states, int count) {
     s->vis_sp_tokens = 0;
 }
 
-// One workgroup per cache; the loop moves at most a page or two.
-__global__ void k_evict(CacheState* states, int count, int sliding_window) {
+// Deferred eviction, one workgroup per cache: first the pending commit of the
+// last appended frame (a keyframe's page joins the scale list while it has
+// fewer than scale_frames pages, else the window; its special tokens join the
+// special stream), then the oldest window pages go to the free list while the
+// window holds more than sliding_window pages.  The target page is still the
+// free-list top (or the next never-used page): nothing changed it since the
+// append.
+__global__ void k_evict(CacheState* states, int count, int scale_frames, int sliding_window,
+                        int max_sp_tokens, int nsp) {
     int c = blockIdx.x;
     if (c >= count || threadIdx.x != 0) return;
     CacheState* s = states + c;
     if (s->status != RPKV_OK) return;
     int n_win = s->n_win, head = s->win_head, n_free = s->n_free;
+    if (s->pending) {
+        s->pending = 0;
+        if (s->n_sp + nsp > max_sp_tokens) {
+            s->status = RPKV_ENOSPACE;
+            return;
+        }
+        const int page = s->target;
+        if (n_free > 0)
+            --n_free;
+        else
+            s->fresh = s->fresh + 1;
+        const int ns = s->n_scale;
+        if (ns < scale_frames) {
+            s->scale[ns] = page;
+            s->n_scale = ns + 1;
+        } else {
+            s->win[(head + n_win) % kMaxPool] = page;
+            ++n_win;
+        }
+        s->n_sp = s->n_sp + nsp;
+    }
     while (n_win > sliding_window) {
         s->free_[n_free++] = s->win[head];
         head = (head + 1) % kMaxPool;
@@ -54,6 +85,13 @@ __global__ void k_evict(CacheState* states, int count, int sliding_window) {
     s->n_win = n_win;
     s->win_head = head;
     s->n_free = n_free;
+}
+
+// Discards the last appended frame: its K/V stay in the tentative slot and are
+// never kept.
+__global__ void k_rollback(CacheState* states, int count) {
+    int c = blockIdx.x;
+    if (c < count && threadIdx.x == 0) states[c].pending = 0;
 }
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
@@ -72,8 +110,15 @@ hipError_t launch_reset(CacheState* states, int count, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_evict(CacheState* states, int count, int sliding_window, hipStream_t st) {
-    hipLaunchKernelGGL(k_evict, dim3(count), dim3(64), 0, st, states, count, sliding_window);
+hipError_t launch_evict(CacheState* states, int count, int scale_frames, int sliding_window,
+                        int max_sp_tokens, int nsp, hipStream_t st) {
+    hipLaunchKernelGGL(k_evict, dim3(count), dim3(64), 0, st, states, count, scale_frames,
+                       sliding_window, max_sp_tokens, nsp);
+    return hipGetLastError();
+}
+
+hipError_t launch_rollback(CacheState* states, int count, hipStream_t st) {
+    hipLaunchKernelGGL(k_rollback, dim3(count), dim3(64), 0, st, states, count);
     return hipGetLastError();
 }
 

@@ -11,12 +11,13 @@
 //  * rotated K and raw V of the patch tokens go to the frame's patch page,
 //    those of the special tokens to the special stream; rotated Q goes to
 //    q_rot for the attention kernel;
-//  * the target page is the free-list top, else the next never-used page; a
-//    keyframe commits it (scale list first, then the window) and its special
-//    tokens, a skip-append frame only writes the tentative slot;
+//  * the target page is the free-list top, else the next never-used page, and
+//    the specials go right after the committed ones: the frame's tentative
+//    slot; the deferred-eviction call later keeps it (keyframe) or not
+//    (skip-append);
 //  * the visible page table is rebuilt: scale pages, window pages oldest
-//    first, the frame's own page if it is tentative, then the special pages
-//    and the last special page's length.
+//    first, the frame's own page, then the special pages and the last special
+//    page's length.
 //
 // Layout of the work: one workgroup per (tile of 64 tokens, head, stream);
 // tile 0 carries the special tokens.  Each thread moves 16-byte chunks, so
@@ -24,8 +25,8 @@
 // full-width coalesced accesses; V goes through LDS to be written transposed
 // (the layout the attention kernel's matrix-core operands read).  The
 // bookkeeping never leaves the device: every workgroup derives the target page
-// from the state as it stands, and the last workgroup to arrive (atomic
-// ticket) commits the new state.
+// from the state as it stands (which no workgroup of the launch modifies), and
+// one workgroup per stream writes the frame record -- no atomics, no fences.
 #include "rpkv_internal.h"
 
 namespace rpkv {
@@ -102,7 +103,6 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
     constexpr int NCH = kTile * CPR;       // chunks per tile and tensor
     constexpr int PER = NCH / 256;         // chunks per thread
     __shared__ T vt[kTile][kHeadDim + CH];
-    __shared__ int s_last;
 
     const int tile = blockIdx.x, h = blockIdx.y, s = blockIdx.z, tid = threadIdx.x;
     CacheState* st = a.states + s;
@@ -113,8 +113,9 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
     const int fresh = st->fresh;
     const int page = n_free > 0 ? st->free_[n_free - 1] : fresh;
     const int sp_off = st->n_sp;
-    const bool ok = status == RPKV_OK && (n_free > 0 || fresh < a.pool) &&
-                    (!a.commit || sp_off + a.nsp <= a.max_kf * a.nsp);
+    // The special stream always has room for one frame beyond the committed
+    // ones; its capacity is checked when the frame is committed.
+    const bool ok = status == RPKV_OK && (n_free > 0 || fresh < a.pool);
 
     const bool special = tile == 0;
     const int slot0 = special ? 0 : (tile - 1) * kTile;
@@ -189,51 +190,28 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
         }
     }
 
-    // Arrival: the last workgroup of this stream commits the bookkeeping.
-    __syncthreads();
-    if (tid == 0) {
-        __threadfence();
-        const int t = atomicAdd(&st->ticket, 1);
-        s_last = (t == a.n_tiles * a.H - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-
-    // Visible patch pages: old scale pages, old window oldest first, then the
-    // frame's page (committed to the scale list or the window, or tentative:
-    // in every case it comes last).
+    // Frame record, written by one workgroup per stream: the visible table
+    // this frame's attention reads, and the pending commit that the deferred
+    // eviction call applies.  It touches only fields no workgroup of this
+    // launch reads (the structural state above is left as it is), so no
+    // workgroup waits for another.
+    if (tile != 0 || h != 0) return;
+    // Visible patch pages: scale pages, window oldest first, then the frame's
+    // own page (it comes last whether it will be committed or not).
     const int ns = st->n_scale, nw = st->n_win, head = st->win_head;
     const int vis_n = ok ? ns + nw + 1 : 0;
     for (int i = tid; i < vis_n; i += 256)
         st->vis[i] = i < ns ? st->scale[i] : (i < ns + nw ? st->win[(head + i - ns) % kMaxPool] : page);
-    __syncthreads();
     if (tid == 0) {
         if (!ok) {
-            st->status = status != RPKV_OK ? status : RPKV_ENOSPACE;
+            if (status == RPKV_OK) st->status = RPKV_ENOSPACE;
             st->vis_n = 0;
             st->vis_sp_tokens = 0;
             st->vis_sp_pages = 0;
             st->last_page_len = 0;
+            st->pending = 0;
         } else {
-            int vis_sp;
-            if (a.commit) {
-                if (n_free > 0)
-                    st->n_free = n_free - 1;
-                else
-                    st->fresh = fresh + 1;
-                if (ns < a.sf) {
-                    st->scale[ns] = page;
-                    st->n_scale = ns + 1;
-                } else {
-                    st->win[(head + nw) % kMaxPool] = page;
-                    st->n_win = nw + 1;
-                }
-                st->n_sp = sp_off + a.nsp;
-                vis_sp = sp_off + a.nsp;
-            } else {
-                vis_sp = sp_off + a.nsp;
-            }
+            const int vis_sp = sp_off + a.nsp;
             const int sp_pages = (vis_sp + a.sp_page - 1) / a.sp_page;
             st->target = page;
             st->sp_off = sp_off;
@@ -241,8 +219,8 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
             st->vis_sp_tokens = vis_sp;
             st->vis_sp_pages = sp_pages;
             st->last_page_len = sp_pages ? vis_sp - (sp_pages - 1) * a.sp_page : 0;
+            st->pending = a.commit;
         }
-        st->ticket = 0;
     }
 }
 

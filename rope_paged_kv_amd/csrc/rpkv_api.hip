@@ -275,7 +275,15 @@ int attend_frame(kv_handle* h, int layer, const void* q_rot, void* out, float* l
 
 int kv_evict_deferred(kv_handle* h, int layer, void* stream) {
     if (!h || layer < 0 || layer >= h->cfg.num_layers) return RPKV_EINVAL;
-    return hip_status(launch_evict(states_of(h, layer), h->L.S, h->L.W, (hipStream_t)stream));
+    const Layout& L = h->L;
+    return hip_status(launch_evict(states_of(h, layer), L.S, L.sf, L.W, L.max_kf * L.nsp, L.nsp,
+                                   (hipStream_t)stream));
+}
+
+int kv_rollback(kv_handle* h, int layer, void* stream) {
+    if (!h || layer < 0 || layer >= h->cfg.num_layers) return RPKV_EINVAL;
+    if (layer == 0 && h->committed > 0) h->committed--;
+    return hip_status(launch_rollback(states_of(h, layer), h->L.S, (hipStream_t)stream));
 }
 
 int kv_read_state(kv_handle* h, int layer, int stream_idx, kv_state_host* out, void* stream) {
@@ -305,6 +313,7 @@ int kv_read_state(kv_handle* h, int layer, int stream_idx, kv_state_host* out, v
     out->visible_special_pages = tmp->vis_sp_pages;
     out->last_page_len = tmp->last_page_len;
     out->visible_special_tokens = tmp->vis_sp_tokens;
+    out->pending_commit = tmp->pending;
     for (int i = 0; i < tmp->n_free && i < kMaxPool; ++i) out->free_list[i] = tmp->free_[i];
     for (int i = 0; i < tmp->n_scale && i < kMaxPool; ++i) out->scale_pages[i] = tmp->scale[i];
     for (int i = 0; i < tmp->n_win && i < kMaxPool; ++i)

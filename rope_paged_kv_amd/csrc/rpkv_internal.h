@@ -13,10 +13,11 @@ constexpr int kTile = 64;         // keys per attention tile, slots per append t
 constexpr int kMaxPool = RPKV_MAX_POOL_PAGES;
 
 // Bookkeeping of one (layer, stream) cache, resident in device memory.
-// Written only by the last workgroup of kv_append_frame, by the eviction
-// kernel and by the reset kernel; read by every kernel of the path.
+// Structural fields (free list, scale list, window, counters) change only in
+// the commit/eviction and reset kernels; the append kernel writes the frame
+// record (target, sp_off, pending, visible table); every kernel reads.
 struct CacheState {
-    int ticket;         // arrival counter of the append kernel's workgroups
+    int pending;        // 1: the last appended frame is a keyframe not yet committed
     int status;         // RPKV_OK or RPKV_ENOSPACE (sticky)
     int fresh;          // never-used pages are fresh .. pool-1
     int n_free;         // free list (stack) size
@@ -99,7 +100,9 @@ struct AttnArgs {
 // Launchers (one per translation unit).
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_reset(CacheState* states, int count, hipStream_t st);
-hipError_t launch_evict(CacheState* states, int count, int sliding_window, hipStream_t st);
+hipError_t launch_evict(CacheState* states, int count, int scale_frames, int sliding_window,
+                        int max_sp_tokens, int nsp, hipStream_t st);
+hipError_t launch_rollback(CacheState* states, int count, hipStream_t st);
 hipError_t launch_rope_append(const AppendArgs& a, int dtype, hipStream_t st);
 hipError_t launch_attend(const AttnArgs& a, int dtype, hipStream_t st);
 

@@ -101,30 +101,34 @@ def test_random_keyframe_masks_bit_exact():
             check_after_evict(cache.state(), sim, f)
 
 
-def test_pool_exhaustion_is_sticky_and_reset_recovers():
+def test_append_without_eviction_and_rollback():
+    """Appends not followed by kv_evict_deferred replace each other in the
+    tentative slot; kv_rollback drops a frame; both agree with the simulator."""
     wl = small_variants()["small_bf16"]
     cache = make_cache(wl)
     run = Runner(wl, cache)
     z = torch.zeros((1, wl.tokens, wl.heads, wl.head_dim), dtype=run.dt, device="cuda")
-    pool = wl.scale_frames + wl.sliding_window + 1
-    for f in range(pool):                       # no eviction: the pool fills up
-        cache.append(0, f, 1, z, z, z, run.q_rot)
-    assert cache.state()["status"] == 0
-    cache.append(0, pool, 1, z, z, z, run.q_rot)
-    st = cache.state()
-    assert st["status"] == rp.RPKV_ENOSPACE and st["n_visible_pages"] == 0
-    cache.attend(0, run.q_rot, run.out, run.lse)     # empty visible set: zeros, lse -inf
-    assert torch.all(run.out == 0) and torch.all(torch.isneginf(run.lse))
-    cache.evict(0)
-    cache.append(0, pool + 1, 1, z, z, z, run.q_rot)
-    assert cache.state()["status"] == rp.RPKV_ENOSPACE
-    cache.reset(0)
-    cache.append(0, 0, 1, z, z, z, run.q_rot)
-    st = cache.state()
-    assert st["status"] == 0 and st["target_page"] == 0 and st["visible_pages"] == [0]
+    sim = sim_for(wl)
+    script = [(0, 1, "evict"), (1, 1, "none"), (2, 1, "none"), (3, 1, "evict"), (4, 1, "rollback"),
+              (5, 0, "evict"), (6, 1, "rollback"), (7, 1, "evict"), (8, 1, "evict"), (9, 1, "evict"),
+              (10, 1, "rollback"), (11, 1, "evict")]
+    for f, c, act in script:
+        sim.append(f, bool(c))
+        cache.append(0, f, c, z, z, z, run.q_rot)
+        st = cache.state()
+        check_state(st, sim, f)
+        assert st["pending_commit"] == int(sim.pending is not None), f
+        if act == "evict":
+            sim.evict()
+            cache.evict(0)
+        elif act == "rollback":
+            sim.rollback()
+            cache.rollback(0)
+        check_after_evict(cache.state(), sim, f)
+        assert cache.state()["pending_commit"] == int(sim.pending is not None), f
 
 
-def test_special_stream_overflow():
+def test_special_stream_overflow_is_sticky_and_reset_recovers():
     wl = small_variants()["small_bf16"]
     cache = make_cache(wl, max_keyframes=3)
     run = Runner(wl, cache)
@@ -132,10 +136,22 @@ def test_special_stream_overflow():
     for f in range(3):
         cache.append(0, f, 1, z, z, z, run.q_rot)
         cache.evict(0)
-    cache.append(0, 3, 0, z, z, z, run.q_rot)          # tentative: still fits
+    cache.append(0, 3, 0, z, z, z, run.q_rot)          # tentative: always fits
+    cache.evict(0)
     assert cache.state()["status"] == 0
     cache.append(0, 4, 1, z, z, z, run.q_rot)
-    assert cache.state()["status"] == rp.RPKV_ENOSPACE
+    cache.evict(0)                                       # a 4th keyframe does not fit
+    st = cache.state()
+    assert st["status"] == rp.RPKV_ENOSPACE and st["n_special_tokens"] == 18
+    cache.append(0, 5, 1, z, z, z, run.q_rot)          # sticky: nothing written, nothing visible
+    st = cache.state()
+    assert st["status"] == rp.RPKV_ENOSPACE and st["n_visible_pages"] == 0
+    cache.attend(0, run.q_rot, run.out, run.lse)       # empty visible set: zeros, lse -inf
+    assert torch.all(run.out == 0) and torch.all(torch.isneginf(run.lse))
+    cache.reset(0)
+    cache.append(0, 0, 1, z, z, z, run.q_rot)
+    st = cache.state()
+    assert st["status"] == 0 and st["target_page"] == 0 and st["visible_pages"] == [0]
 
 
 # ---------------------------------------------------------------- RoPE + pages
@@ -272,7 +288,7 @@ def test_visibility_probe_q_zero():
         run.frame(f, q, k, to_dev(v, run.dt), commit, evict=False)
         sim.append(f, commit)
         pf = sim.visible_patch_frames(f)
-        spf = sim.special_frames + ([] if commit else [f])
+        spf = sim.special_frames + [f]
         total = len(pf) * wl.patches + len(spf) * wl.n_special
         want0 = np.zeros(64)
         want1 = np.zeros(64)

@@ -90,7 +90,7 @@ def test_visibility_probe_against_page_simulator(name):
     for f in range(wl.frames):
         sim.append(f, wl.is_keyframe(f))
         pf = sim.visible_patch_frames(f)
-        spf = sim.special_frames + ([] if wl.is_keyframe(f) else [f])
+        spf = sim.special_frames + [f]
         total = len(pf) * wl.patches + len(spf) * wl.n_special
         want0 = np.zeros(wl.head_dim)
         want1 = np.zeros(wl.head_dim)

@@ -2,6 +2,7 @@
 fixtures (tests/golden), the closed form of the page id of a stored frame,
 structural invariants, and the cross-check between the two independent
 descriptions (pages vs. direct enumeration)."""
+import collections
 import os
 import random
 
@@ -71,15 +72,19 @@ def test_partial_special_pages_trace():
 def test_long_stream_transitions():
     wl = WORKLOADS[2]
     want = {int(r[0]): r for r in _rows("long_stream_transitions.txt")}
-    for f, c, sim in run_sim(wl):
+    sim = pages.PageSim(wl.scale_frames, wl.sliding_window, wl.special_page_size, wl.n_special)
+    for f in range(wl.frames):
+        c = wl.is_keyframe(f)
+        sim.append(f, c)
+        vis = sim.visible
+        freed = sim.evict()
         if f in want:
             r = want[f]
             assert sim.target == int(r[1]) and c == bool(int(r[2]))
-            assert len(sim.visible.patch_pages) == int(r[3])
-            assert sim.visible.special_pages == int(r[5]) and sim.visible.last_page_len == 6
-            ev = list(sim.window)[:max(0, len(sim.window) - wl.sliding_window)]
-            assert ev == _ints(r[4])
-    assert sim.visible.special_tokens == 1236 and sim.n_sp == 1230
+            assert len(vis.patch_pages) == int(r[3])
+            assert vis.special_pages == int(r[5]) and vis.last_page_len == 6
+            assert freed == _ints(r[4])
+    assert vis.special_tokens == 1236 and sim.n_sp == 1230
     assert sim.fresh == 73 and sim.free == [10]
 
 
@@ -105,7 +110,7 @@ def test_pages_agree_with_enumeration(cid):
         assert sim.visible_patch_frames(f) == pf
         want_sp = len(spf) * wl.n_special
         assert sim.visible.special_tokens == want_sp
-        assert sim.special_frames + ([] if c else [f]) == spf
+        assert sim.special_frames + [f] == spf
 
 
 def test_random_keyframe_masks_agree_and_invariants():
@@ -130,7 +135,7 @@ def test_random_keyframe_masks_agree_and_invariants():
             assert (vis.special_pages - 1) * spp + vis.last_page_len == vis.special_tokens
             scale_before = list(sim.scale)
             sim.evict()
-            assert len(sim.window) <= w and sim.scale == scale_before
+            assert len(sim.window) <= w and sim.scale[:len(scale_before)] == scale_before
             used = set(sim.scale) | set(sim.window)
             assert not (used & set(sim.free))
             assert used | set(sim.free) | set(range(sim.fresh, sf + w + 1)) == pool
@@ -138,23 +143,42 @@ def test_random_keyframe_masks_agree_and_invariants():
                 stored.append(f)
 
 
-def test_pool_exhaustion_without_eviction():
+def test_append_without_eviction_replaces_the_pending_frame():
     sim = pages.PageSim(1, 2, 6, 6)       # pool of 4 pages
-    for f in range(4):
+    for f in range(6):                    # never evicted: nothing is kept
         assert sim.append(f, True) == pages.OK
-    assert sim.append(4, True) == pages.ENOSPACE
-    assert sim.append(5, True) == pages.ENOSPACE      # sticky
-    sim.reset()
-    assert sim.append(0, True) == pages.OK and sim.target == 0
+        assert sim.target == 0 and sim.visible.patch_pages == [0]
+    sim.evict()                           # keeps frame 5 only
+    assert sim.scale == [0] and sim.page_frame == {0: 5} and sim.special_frames == [5]
+
+
+def test_rollback_drops_the_frame():
+    sim = pages.PageSim(1, 2, 6, 6)
+    sim.append(0, True)
+    sim.evict()
+    sim.append(1, True)
+    sim.rollback()
+    sim.evict()
+    assert sim.window == collections.deque() and sim.n_sp == 6
+    sim.append(2, True)
+    assert sim.target == 1
+    sim.evict()
+    assert list(sim.window) == [1] and sim.page_frame[1] == 2
 
 
 def test_special_capacity_overflow():
     sim = pages.PageSim(1, 2, 6, 6, special_capacity=12)
-    assert sim.append(0, True) == pages.OK
+    for f in range(2):
+        assert sim.append(f, True) == pages.OK
+        sim.evict()
+    assert sim.append(2, False) == pages.OK        # the tentative slot always fits
     sim.evict()
-    assert sim.append(1, True) == pages.OK
-    sim.evict()
-    assert sim.append(2, False) == pages.ENOSPACE
+    assert sim.append(3, True) == pages.OK
+    sim.evict()                                    # keeping it would exceed 12 tokens
+    assert sim.status == pages.ENOSPACE
+    assert sim.append(4, True) == pages.ENOSPACE   # sticky
+    sim.reset()
+    assert sim.append(0, True) == pages.OK and sim.target == 0
 
 
 def test_keyframe_storage_reduction():
