@@ -9,6 +9,7 @@ import glob
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -20,21 +21,23 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # packed fp32 instructions stay off: the compiler must not emit them
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs (no AGPR copies around the
+    # softmax that reads them)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
+# Attention only: its data holds no NaN (masked scores are -inf), so min/max
+# need no NaN quieting and fold into v_max3.
+EXTRA = {"k_attend.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-           *sources(), "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,6 +47,19 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
+
+
+def build(verbose: bool = False) -> str:
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
+    with tempfile.TemporaryDirectory() as tmpd:
+        objs = []
+        for src in sources():
+            obj = os.path.join(tmpd, os.path.basename(src) + ".o")
+            _run([HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), *inc, "-c", src, "-o", obj],
+                 verbose)
+            objs.append(obj)
+        tmp = LIB + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 
