@@ -104,7 +104,20 @@ def main():
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3])
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (3 times) and exit: "
+                         "the reference for scaling HBM byte counters")
     args = ap.parse_args()
+    if args.calibration_copy_mb:
+        import torch
+        n = args.calibration_copy_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n, "copies": 3}))
+        return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               f"(streams and heads shard without communication: run one process per GPU)",

@@ -30,7 +30,7 @@ FLAGS = [
 ]
 # Attention only: its data holds no NaN (masked scores are -inf), so min/max
 # need no NaN quieting and fold into v_max3.
-EXTRA = {"k_attend.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+EXTRA = {"k_attend_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def sources():

@@ -105,5 +105,6 @@ hipError_t launch_evict(CacheState* states, int count, int scale_frames, int sli
 hipError_t launch_rollback(CacheState* states, int count, hipStream_t st);
 hipError_t launch_rope_append(const AppendArgs& a, int dtype, hipStream_t st);
 hipError_t launch_attend(const AttnArgs& a, int dtype, hipStream_t st);
+hipError_t launch_attend_bf16_main(const AttnArgs& a, hipStream_t st);
 
 }  // namespace rpkv
