@@ -1,0 +1,87 @@
+"""Full-depth streaming driver: a stack of attention layers alternating frame
+layers (attention over the frame's own tokens, nothing retained) and global
+layers (attention over the dual-stream paged cache), for several independent
+streams batched in every call.
+
+Per layer: [Q | K | V] = bf16(x) @ W_l (torch GEMM: the projection is the
+model's, not part of the hot path), then the library's RoPE + append,
+attention and (global layers) deferred eviction, then the residual
+x <- x + O in fp32.  Frame and global blocks are named on page "How
+LingBot-Map Achieves Real-Time 3D Reconstruction", section "AggregatorStream
+with FlashInfer Paged KV Cache"; the block internals need trained weights,
+so this driver keeps only the projection, the attention and the residual.
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+import torch
+
+from . import PagedKVCache, make_config, make_spec
+
+
+class FullDepthStream:
+    def __init__(self, *, streams: int, layers: int, heads: int, grid_h: int, grid_w: int,
+                 scale_frames: int, sliding_window: int, keyframe_interval: int, frames: int,
+                 weights: List[torch.Tensor], head_dim: int = 64, special_tokens: int = 6,
+                 pairs=(12, 10, 10), theta: float = 10000.0, ntk_factor: float = 1.0,
+                 attn_splits: int = 0, device="cuda"):
+        if layers % 2:
+            raise ValueError("layers alternate frame/global: an even count is expected")
+        self.S, self.L, self.H, self.D = streams, layers, heads, head_dim
+        self.N = special_tokens + grid_h * grid_w
+        self.hidden = heads * head_dim
+        self.interval = keyframe_interval
+        self.device = torch.device(device)
+        spec = make_spec(head_dim=head_dim, pairs=pairs, theta=theta, ntk_factor=ntk_factor,
+                         max_frames=frames, max_h=grid_h, max_w=grid_w)
+        common = dict(num_streams=streams, num_heads=heads, grid_h=grid_h, grid_w=grid_w,
+                      dtype="bf16", head_dim=head_dim, special_tokens=special_tokens, rope=spec)
+        # Frame layers keep nothing: every append is a skip-append on a cache
+        # with no scale pages and no window, so one handle serves all of them.
+        self.frame_cache = PagedKVCache(make_config(num_layers=1, scale_frames=0, sliding_window=0,
+                                                    max_keyframes=0, attn_splits=1, **common),
+                                        device=self.device)
+        n_kf = (frames + keyframe_interval - 1) // keyframe_interval
+        self.global_cache = PagedKVCache(make_config(num_layers=layers // 2,
+                                                     scale_frames=scale_frames,
+                                                     sliding_window=sliding_window,
+                                                     max_keyframes=n_kf, attn_splits=attn_splits,
+                                                     **common), device=self.device)
+        # W_l split into its Q, K, V thirds (contiguous, so each GEMM writes a
+        # contiguous [S*N, H*D] = [S][N][H][D] tensor).
+        self.w = [tuple(wl[:, i * self.hidden:(i + 1) * self.hidden].contiguous() for i in range(3))
+                  for wl in weights]
+        shape = (streams, self.N, heads, head_dim)
+        mk = lambda: torch.empty(shape, dtype=torch.bfloat16, device=self.device)
+        self.q, self.k, self.v, self.q_rot, self.out = mk(), mk(), mk(), mk(), mk()
+
+    def reset(self):
+        self.global_cache.reset(-1)
+        self.frame_cache.reset(-1)
+
+    def frame(self, f: int, x: torch.Tensor, keep: Optional[List[torch.Tensor]] = None) -> torch.Tensor:
+        """Runs frame f (x: fp32 [S][N][hidden], updated in place) through all
+        layers; appends each layer's attention output to `keep` if given."""
+        rows = self.S * self.N
+        commit = int(f % self.interval == 0)
+        for layer in range(self.L):
+            xb = x.view(rows, self.hidden).to(torch.bfloat16)
+            wq, wk, wv = self.w[layer]
+            torch.mm(xb, wq, out=self.q.view(rows, self.hidden))
+            torch.mm(xb, wk, out=self.k.view(rows, self.hidden))
+            torch.mm(xb, wv, out=self.v.view(rows, self.hidden))
+            if layer % 2 == 0:
+                c = self.frame_cache
+                c.append(0, f, 0, self.q, self.k, self.v, self.q_rot)
+                c.attend(0, self.q_rot, self.out)
+            else:
+                g = layer // 2
+                c = self.global_cache
+                c.append(g, f, commit, self.q, self.k, self.v, self.q_rot)
+                c.attend(g, self.q_rot, self.out)
+                c.evict(g)
+            if keep is not None:
+                keep.append(self.out.clone())
+            x.add_(self.out.view(self.S, self.N, self.hidden).float())
+        return x

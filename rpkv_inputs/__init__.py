@@ -162,6 +162,13 @@ def qkv(wl: Workload, layer: int, stream: int, frame: int, tensor: int) -> np.nd
     return _store(wl, x)
 
 
+def qkv_layer(wl: Workload, layer: int, stream: int, frame: int, tensor: int) -> np.ndarray:
+    """Layer-distinct inputs without drawing new numbers: the layer-0 draw of
+    the (stream, frame, tensor) rolled by `layer` positions along the head axis
+    (used where many layers would make fresh draws too slow)."""
+    return np.roll(qkv(wl, 0, stream, frame, tensor), layer, axis=1)
+
+
 def frame_qkv(wl: Workload, layer: int, frame: int, streams: Optional[Sequence[int]] = None):
     """(q, k, v) for one frame and all streams: each float32 [S, N, H, D]."""
     ss = range(wl.streams) if streams is None else streams
