@@ -22,8 +22,9 @@ Every appended frame first goes to the *tentative slot* -- the page the next
 stored frame would take and the special tokens right after the stored ones --
 where its own attention sees it; the deferred-eviction call keeps it if it is
 a keyframe, a rollback (or skip-append) drops it (page "KV Caching Benefits in
-Ling Bot-Map", section "Dynamic Keyframe Selection": the deferred eviction
-retains the current KV, the rollback removes the temporary entry).
+Ling Bot-Map", section "Dynamic Keyframe Selection": the deferred-eviction
+call is what keeps a keyframe's KV, and a rollback discards the temporary
+entry).
 
 Readings (the pages are silent): the free list is a stack (last in, first
 out); the frame being processed is listed after the window.  The free

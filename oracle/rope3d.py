@@ -15,8 +15,8 @@ KV-Cache Streaming"):
   (theta * ntk)^(-2j / d_a), j < d_a/2 (the pages name theta and the NTK factor
   that multiplies it, not the formula: reading, textbook RoPE);
 * the complex table multiplies the feature vector viewed as head_dim/2 complex
-  numbers x_{2j} + i x_{2j+1} (adjacent pairs: reading of "complex tensor
-  [..., head_dim//2]" applied with real arithmetic);
+  numbers x_{2j} + i x_{2j+1} (adjacent pairs: the plainest reading of a
+  complex table of head_dim/2 entries per token applied with real arithmetic);
 * the temporal coordinate of a frame is its global frame index; the 6 special
   tokens that precede the patches sit at (t, 0, 0) (reading: only the temporal
   rotation, as for the camera head's 1x1 grid); patch token p sits at

@@ -60,9 +60,12 @@ class FullDepthStream:
         self.global_cache.reset(-1)
         self.frame_cache.reset(-1)
 
-    def frame(self, f: int, x: torch.Tensor, keep: Optional[List[torch.Tensor]] = None) -> torch.Tensor:
+    def frame(self, f: int, x: torch.Tensor, keep: Optional[List[torch.Tensor]] = None,
+              events: Optional[list] = None) -> torch.Tensor:
         """Runs frame f (x: fp32 [S][N][hidden], updated in place) through all
-        layers; appends each layer's attention output to `keep` if given."""
+        layers; appends each layer's attention output to `keep` if given, and
+        (frame, layer, start event, end event) around each attention launch to
+        `events` if given."""
         rows = self.S * self.N
         commit = int(f % self.interval == 0)
         for layer in range(self.L):
@@ -71,15 +74,16 @@ class FullDepthStream:
             torch.mm(xb, wq, out=self.q.view(rows, self.hidden))
             torch.mm(xb, wk, out=self.k.view(rows, self.hidden))
             torch.mm(xb, wv, out=self.v.view(rows, self.hidden))
-            if layer % 2 == 0:
-                c = self.frame_cache
-                c.append(0, f, 0, self.q, self.k, self.v, self.q_rot)
-                c.attend(0, self.q_rot, self.out)
-            else:
-                g = layer // 2
-                c = self.global_cache
-                c.append(g, f, commit, self.q, self.k, self.v, self.q_rot)
-                c.attend(g, self.q_rot, self.out)
+            c, g, cm = (self.frame_cache, 0, 0) if layer % 2 == 0 else (self.global_cache, layer // 2, commit)
+            c.append(g, f, cm, self.q, self.k, self.v, self.q_rot)
+            if events is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+            c.attend(g, self.q_rot, self.out)
+            if events is not None:
+                e1.record()
+                events.append((f, layer, e0, e1))
+            if layer % 2 == 1:
                 c.evict(g)
             if keep is not None:
                 keep.append(self.out.clone())

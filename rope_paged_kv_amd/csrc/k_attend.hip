@@ -112,11 +112,26 @@ __global__ __launch_bounds__(64) void k_attend_f32(AttnArgs a) {
         int vstride, len;
         tile_ref<float>(a, s, h, t, n_patch_tiles, st->vis, vis_sp, kp, vp, vstride, len);
         __syncthreads();
-        for (int i = tid; i < kTile * kHeadDim; i += 64) {
-            const int r = i / kHeadDim, d = i % kHeadDim;
-            ks[r][d] = kp[(size_t)r * kHeadDim + d];
-            const int vr = i / kTile, vc = i % kTile;
-            vs[vr][vc] = vp[(size_t)vr * vstride + vc];
+        // 16-byte loads, all issued before the LDS stores: thread tid takes
+        // float4 chunks tid, tid+64, ... of the K tile and of the V^T tile.
+        float4 kr[16], vr[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int i = tid + 64 * j;          // chunk: row i/16, columns 4*(i%16)..+3
+            kr[j] = *(const float4*)(kp + (size_t)(i >> 4) * kHeadDim + 4 * (i & 15));
+            vr[j] = *(const float4*)(vp + (size_t)(i >> 4) * vstride + 4 * (i & 15));
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int i = tid + 64 * j, r = i >> 4, c4 = 4 * (i & 15);
+            ks[r][c4] = kr[j].x;
+            ks[r][c4 + 1] = kr[j].y;
+            ks[r][c4 + 2] = kr[j].z;
+            ks[r][c4 + 3] = kr[j].w;
+            vs[r][c4] = vr[j].x;
+            vs[r][c4 + 1] = vr[j].y;
+            vs[r][c4 + 2] = vr[j].z;
+            vs[r][c4 + 3] = vr[j].w;
         }
         __syncthreads();
         for (int j = 0; j < len; ++j) {
