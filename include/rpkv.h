@@ -151,7 +151,10 @@ typedef struct {
 
 typedef struct kv_handle kv_handle;
 
-/* Bytes of device memory kv_create needs for `cfg`; 0 if cfg is invalid. */
+/* Bytes of device memory kv_create needs for `cfg`; 0 if cfg is invalid.
+ * Besides the field limits above, a bf16 cache is invalid when one head's
+ * patch pool or special stream would reach 4 GiB (the attention kernel
+ * addresses a head through 32-bit buffer offsets). */
 size_t kv_required_bytes(const kv_config* cfg);
 
 /* Lays the cache out in the caller's d_mem (>= kv_required_bytes, 256-byte

@@ -15,17 +15,21 @@
 //  * keys are walked in tiles of 64 that never straddle a page (a patch page
 //    of P tokens is ceil(P/64) tiles; the special stream, whose pages are
 //    appended in order and never evicted, is contiguous per head);
-//  * tiles stream from HBM straight into LDS (global_load_lds_dwordx4: no
-//    staging registers) through a 4-stage ring, two tiles ahead, one barrier
-//    per tile; 16-byte chunks are XOR-swizzled so operand reads hit 64
-//    distinct banks;
+//  * tiles stream from HBM straight into LDS (buffer_load ... lds: no staging
+//    registers, the page offset in a scalar register) through a ring of
+//    stages, one barrier per tile; 16-byte chunks are XOR-swizzled so operand
+//    reads hit 64 distinct banks;
 //  * scores are formed transposed, S^T = K Q^T (keys on the MFMA rows, queries
-//    on the columns): each lane holds 32 scores of one query, so the softmax
-//    statistics stay in-lane but for one exchange with the lane 32 apart;
-//    P^T rounded to bf16 is directly the B operand of O^T = V^T P^T, V being
-//    stored transposed in the cache in the key order this layout produces;
-//  * each pair of output products follows the exponentials of its 16 keys,
-//    so the matrix core works on one batch while the next is exponentiated;
+//    on the columns): each lane holds 16 scores of one query per 32-key half
+//    tile, so the softmax statistics stay in-lane but for one exchange with
+//    the lane 32 apart; P^T rounded to bf16 is directly the B operand of
+//    O^T = V^T P^T, V being stored transposed in the cache in the key order
+//    this layout produces;
+//  * the wave is software-pipelined by half tiles: the score products of the
+//    next half are issued before the exponentials of the current one, so the
+//    matrix core and the vector ALU work side by side (the next half of the
+//    last half tile of tile i is the first half of tile i+1, formed after the
+//    barrier of tile i+1);
 //  * Q is pre-multiplied by log2(e)/sqrt(D) and the score accumulators start
 //    at -M (the running reference max), so a product is already the base-2
 //    exponent and p = exp2(t) costs one transcendental; M moves (and the
@@ -38,15 +42,22 @@ namespace rpkv {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
+#ifndef RPKV_ATTN_STAGES
+#define RPKV_ATTN_STAGES 3
+#endif
 constexpr int kWaves = 4;
 constexpr int kQW = 32;                          // queries per wave
 constexpr int kQB = kWaves * kQW;                // queries per workgroup
-constexpr int kStages = 4;
+constexpr int kStages = RPKV_ATTN_STAGES;        // LDS ring; tile i+kStages-2 loads during tile i
 constexpr int kTileBytes = kTile * kHeadDim * 2; // one 64x64 bf16 tile: 8 KB
 constexpr int kStageBytes = 2 * kTileBytes;      // K tile + V^T tile
-
+constexpr int kHalfBytes = 32 * 128;             // 32 rows of a tile
+// Word 3 of a raw (unstructured) buffer resource on gfx9: 32-bit data format.
+constexpr int kBufWord3 = 0x00020000;
+static_assert(kStages >= 3, "tile i is still read after the barrier of tile i+1");
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
 // 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
@@ -57,189 +68,166 @@ __device__ inline void wait_vmcnt() {
 
 __device__ inline float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
-// Position in the tile sequence of a split: patch page index pi (pi == vis_n:
-// the special stream) and tile ti within it.
-struct Cursor {
-    int pi, ti;
-};
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-struct Walk {
-    const uint16_t* kbase;   // this (stream, head): K pool, V^T pool, K / V^T specials
-    const uint16_t* vbase;
-    const uint16_t* kspb;
-    const uint16_t* vspb;
-    const int* vis;          // visible pages (LDS copy)
-    int tpp, P, vis_n, vis_sp, slot_cap, sp_cap;
-
-    __device__ Cursor at(int t) const {
-        const int npt = vis_n * tpp;
-        if (t < npt) return {t / tpp, t % tpp};
-        return {vis_n, t - npt};
-    }
-    __device__ void next(Cursor& c) const {
-        ++c.ti;
-        if (c.pi < vis_n && c.ti == tpp) {
-            ++c.pi;
-            c.ti = 0;
-        }
-    }
-    __device__ int len(const Cursor& c) const {
-        return min(kTile, (c.pi < vis_n ? P : vis_sp) - c.ti * kTile);
-    }
-    // Issues this wave's share of the loads of tile c into an LDS stage: rows
-    // 16*wave .. 16*wave+15 of the K tile and of the V^T tile, 8 rows per
-    // instruction.  k0/k1 (v*0/v*1) are this lane's byte offsets inside the
-    // two 8-row slabs: its row, and the 16-byte chunk that belongs at its slot
-    // under the swizzle.
-    __device__ void issue(const Cursor& c, char* stage, int wave, uint32_t k0, uint32_t k1,
-                          uint32_t vpage0, uint32_t vpage1, uint32_t vsp0, uint32_t vsp1) const {
-        const int off = c.ti * kTile;
-        const char* kp;
-        const char* vp;
-        uint32_t v0, v1;
-        if (c.pi < vis_n) {
-            const int page = __builtin_amdgcn_readfirstlane(vis[c.pi]);
-            kp = (const char*)(kbase + ((size_t)page * slot_cap + off) * kHeadDim);
-            vp = (const char*)(vbase + (size_t)page * kHeadDim * slot_cap + off);
-            v0 = vpage0;
-            v1 = vpage1;
-        } else {
-            kp = (const char*)(kspb + (size_t)off * kHeadDim);
-            vp = (const char*)(vspb + off);
-            v0 = vsp0;
-            v1 = vsp1;
-        }
-        char* s0 = stage + wave * 2 * 8 * 128;
-        __builtin_amdgcn_global_load_lds(kp + k0, (lds_void_ptr)s0, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(kp + k1, (lds_void_ptr)(s0 + 8 * 128), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vp + v0, (lds_void_ptr)(s0 + kTileBytes), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vp + v1, (lds_void_ptr)(s0 + kTileBytes + 8 * 128), 16, 0, 0);
-    }
-};
-
-// Reads the eight 16-byte operand fragments of one swizzled 64x64 tile that
-// this lane needs (rows col and 32+col, chunks 2*j+hh).
-__device__ inline void read_frags(const char* tile, const int* off, bf16x8* f) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        f[j] = *(const bf16x8*)(tile + off[j]);
-        f[4 + j] = *(const bf16x8*)(tile + 32 * 128 + off[j]);
-    }
+// Raw buffer resource over [p, p + bytes), built from scalar registers.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_over(const char* p, size_t bytes) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = (uint32_t)uniform((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)uniform((int)(uint32_t)(v >> 32));
+    const int n = uniform((int)(uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, kBufWord3);
 }
+
+// Loads of one (stream, head): buffer resources over its K pool, V^T pool and
+// special K / V^T, and this lane's byte offsets inside the 8-row slabs it
+// loads (its row, and the 16-byte chunk that belongs at its slot under the
+// swizzle).  All page arithmetic is scalar.
+struct Loader {
+    __amdgpu_buffer_rsrc_t kpool, vpool, ksp, vsp;
+    const int* vis;          // visible pages (LDS copy)
+    int vis_n, tpp, slot_cap;
+    uint32_t lk0, lk1, lvp0, lvp1, lvs0, lvs1;
+
+    // Issues this wave's share of tile t (rows 16*wave .. 16*wave+15 of the K
+    // tile and of the V^T tile, 8 rows per instruction) into an LDS stage.
+    __device__ void issue(int t, char* stage, int wave) const {
+        char* s0 = stage + wave * 2 * 8 * 128;
+        const int npt = vis_n * tpp;
+        if (t < npt) {
+            const int pi = t / tpp;
+            const uint32_t off = (uint32_t)(t - pi * tpp) * kTile;
+            const uint32_t page = (uint32_t)uniform(vis[pi]);
+            const uint32_t ko = (page * (uint32_t)slot_cap + off) * 128u;
+            const uint32_t vo = page * (uint32_t)slot_cap * 128u + off * 2u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kpool, (lds_void_ptr)s0, 16, lk0, ko, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kpool, (lds_void_ptr)(s0 + 1024), 16, lk1, ko, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vpool, (lds_void_ptr)(s0 + kTileBytes), 16, lvp0, vo, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vpool, (lds_void_ptr)(s0 + kTileBytes + 1024), 16, lvp1, vo,
+                                                     0, 0);
+        } else {
+            const uint32_t off = (uint32_t)(t - npt) * kTile;
+            const uint32_t ko = off * 128u, vo = off * 2u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksp, (lds_void_ptr)s0, 16, lk0, ko, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksp, (lds_void_ptr)(s0 + 1024), 16, lk1, ko, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vsp, (lds_void_ptr)(s0 + kTileBytes), 16, lvs0, vo, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vsp, (lds_void_ptr)(s0 + kTileBytes + 1024), 16, lvs1, vo, 0,
+                                                     0);
+        }
+    }
+};
 
 // Running state of one wave's 32 queries.
 struct Acc {
     f32x16 o0, o1;     // O^T, d rows 0-31 and 32-63
-    f32x16 negM;       // -M in every element: the score accumulators' start
-    float M, l;
+    float lp[4];       // partial row sums
+    float M;           // reference max of the base-2 scores
     bool first;
 };
 
-// Everything one wave does for key tile i: wait for it, hand tile i+3 to the
-// loader, form its scores, softmax, and the output product.
-struct Ctx {
-    const Walk* w;
-    char* lds;
-    const bf16x8* qf;
-    const int* foff;
-    int wave, hh, n;
-    uint32_t lk0, lk1, lvp0, lvp1, lvs0, lvs1;
-};
+// s = c*q.k for the 32 keys of half kb of a tile (rows 32*kb + col of the K
+// tile; chunk 2*j + hh is k-step j).
+__device__ __forceinline__ f32x16 scores(const char* tile, int kb, const int* foff, const bf16x8* qf) {
+    const char* t = tile + kb * kHalfBytes;
+    const bf16x8 k0 = *(const bf16x8*)(t + foff[0]);
+    const bf16x8 k1 = *(const bf16x8*)(t + foff[1]);
+    const bf16x8 k2 = *(const bf16x8*)(t + foff[2]);
+    const bf16x8 k3 = *(const bf16x8*)(t + foff[3]);
+    const f32x16 zero = {};
+    f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[0], zero, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[1], s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k2, qf[2], s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k3, qf[3], s, 0, 0, 0);
+    return s;
+}
 
-__device__ __forceinline__ void step(const Ctx& x, int i, Cursor& ld, Cursor& cp, Acc& A) {
-    // Tile i landed for every wave (tiles i+1, i+2 may still be in flight), and
-    // every wave is done with tile i-1, whose stage now takes tile i+3.
-    if (i + 2 < x.n)
-        wait_vmcnt<8>();
-    else if (i + 1 < x.n)
-        wait_vmcnt<4>();
-    else
-        wait_vmcnt<0>();
-    __syncthreads();
-    if (i + kStages - 1 < x.n) {
-        x.w->issue(ld, x.lds + ((i + kStages - 1) % kStages) * kStageBytes, x.wave, x.lk0, x.lk1,
-                   x.lvp0, x.lvp1, x.lvs0, x.lvs1);
-        x.w->next(ld);
-    }
-    const int len = x.w->len(cp);
-    x.w->next(cp);
-    const char* cur = x.lds + (i % kStages) * kStageBytes;
-
-    // Scores t = c*q.k - M of the tile's 64 keys (two 32-key blocks).
-    bf16x8 frag[8];
-    read_frags(cur, x.foff, frag);
-    f32x16 sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[0], x.qf[0], A.negM, 0, 0, 0);
-    f32x16 sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[4], x.qf[0], A.negM, 0, 0, 0);
+// One half tile: the softmax weights of sc (half kb of `tile`, len valid keys
+// in the tile), their output products, and -- interleaved with them, so the
+// matrix core works while the exponentials run -- the scores of the next half
+// tile into nxt (K rows at knext; the caller makes sure they are loaded, or
+// ignores nxt).  Key of sc[r]: 32*kb + 8*(r/4) + 4*hh + r%4; its V^T column
+// sits at that key's slot, chunk 4*kb + 2*(r/8) + hh.
+__device__ __forceinline__ void step(f32x16& sc, f32x16& nxt, const char* tile, int kb, int len,
+                                     const char* knext, const int* foff, const bf16x8* qf, int hh,
+                                     Acc& A) {
+    if (len < 32 * kb + 32) {   // ragged: keys past the tile's end do not count
+        const int lim = len - 32 * kb - 4 * hh;
 #pragma unroll
-    for (int j = 1; j < 4; ++j) {
-        sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[j], x.qf[j], sc0, 0, 0, 0);
-        sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[4 + j], x.qf[j], sc1, 0, 0, 0);
+        for (int r = 0; r < 16; ++r)
+            if (8 * (r >> 2) + (r & 3) >= lim) sc[r] = -INFINITY;
     }
-    // V^T fragments, read while the scores finish.
-    read_frags(cur + kTileBytes, x.foff, frag);
-
-    // Ragged tile: keys past its end do not count.  Key of sc_kb[r]:
-    // kb*32 + 8*(r/4) + 4*hh + r%4.
-    if (len < kTile) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = 8 * (r >> 2) + 4 * x.hh + (r & 3);
-            if (key >= len) sc0[r] = -INFINITY;
-            if (32 + key >= len) sc1[r] = -INFINITY;
-        }
-    }
-    // Four independent max chains over 8 scores each, then combined.
-    float m4[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const f32x16& sc = g < 2 ? sc0 : sc1;
-        const int r0 = (g & 1) * 8;
-        float m = max3f(sc[r0], sc[r0 + 1], sc[r0 + 2]);
-        m = max3f(m, sc[r0 + 3], sc[r0 + 4]);
-        m = max3f(m, sc[r0 + 5], sc[r0 + 6]);
-        m4[g] = fmaxf(m, sc[r0 + 7]);
-    }
-    const float mx = max3f(m4[0], m4[1], fmaxf(m4[2], m4[3]));
-    if (A.first || __any(mx > 8.f)) {
+    const float ma = max3f(sc[0], sc[1], sc[2]);
+    const float mb = max3f(sc[3], sc[4], sc[5]);
+    const float mc = max3f(sc[6], sc[7], sc[8]);
+    const float md = max3f(sc[9], sc[10], sc[11]);
+    const float me = max3f(sc[12], sc[13], sc[14]);
+    const float mx = max3f(max3f(ma, mb, mc), fmaxf(md, me), sc[15]);
+    if (A.first || __any(mx > A.M + 8.f)) {
         // rare: move M (jointly for both lanes of a query; never down after
-        // the first tile) and rescale what was accumulated.
+        // the first half tile) and rescale what was accumulated.
         const float d = fmaxf(mx, __shfl_xor(mx, 32));
-        const float shift = A.first ? d : fmaxf(d, 0.f);
+        const float m_new = A.first ? d : fmaxf(d, A.M);
+        const float alpha = A.first ? 0.f : __builtin_amdgcn_exp2f(A.M - m_new);
         A.first = false;
-        A.M += shift;
-        const float alpha = __builtin_amdgcn_exp2f(-shift);
-        A.l *= alpha;
+        A.M = m_new;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) A.lp[e] *= alpha;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             A.o0[r] *= alpha;
             A.o1[r] *= alpha;
-            sc0[r] -= shift;
-            sc1[r] -= shift;
-            A.negM[r] = -A.M;
         }
     }
-
-    // Weights p = exp2(t) of 16 keys at a time, each batch followed by its
-    // two output products; the row sum (four independent partial sums) uses
-    // the bf16 weights the products use.
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float lp[4] = {0.f, 0.f, 0.f, 0.f};
+    // LDS operands: V^T fragments of this half, K fragments of the next.
+    const char* vt = tile + kTileBytes;
+    bf16x8 v[2][2], k[4];
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-        const f32x16& sc = kc < 2 ? sc0 : sc1;
-        const int r0 = (kc & 1) * 8;
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)__builtin_amdgcn_exp2f(sc[r0 + e]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bf16x2 pr = {pb[2 * e], pb[2 * e + 1]};
-            lp[e] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lp[e], false);
-        }
-        A.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[kc], pb, A.o0, 0, 0, 0);
-        A.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[4 + kc], pb, A.o1, 0, 0, 0);
+    for (int m = 0; m < 2; ++m) {
+        v[m][0] = *(const bf16x8*)(vt + foff[2 * kb + m]);
+        v[m][1] = *(const bf16x8*)(vt + kHalfBytes + foff[2 * kb + m]);
     }
-    A.l += (lp[0] + lp[1]) + (lp[2] + lp[3]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k[j] = *(const bf16x8*)(knext + foff[j]);
+    // p = exp2(t), rounded to bf16 in pairs for the products; the row sums
+    // add the fp32 weights (plain adds: the bf16 dot instruction would hold
+    // up the matrix core).
+    bf16x2 pr[8];
+    const f32x16 zero = {};
+#define RPKV_EXP_PAIR(e)                                                                           \
+    do {                                                                                           \
+        const f32x2 x_ = {__builtin_amdgcn_exp2f(sc[2 * (e)] - A.M),                               \
+                          __builtin_amdgcn_exp2f(sc[2 * (e) + 1] - A.M)};                          \
+        pr[e] = __builtin_convertvector(x_, bf16x2);                                               \
+        A.lp[(e) & 3] += x_[0] + x_[1];                                                            \
+    } while (0)
+    nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[0], qf[0], zero, 0, 0, 0);
+    RPKV_EXP_PAIR(0);
+    RPKV_EXP_PAIR(1);
+    nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[1], qf[1], nxt, 0, 0, 0);
+    RPKV_EXP_PAIR(2);
+    RPKV_EXP_PAIR(3);
+    const bf16x8 pb0 = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
+                                               __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
+    nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[2], qf[2], nxt, 0, 0, 0);
+    A.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[0][0], pb0, A.o0, 0, 0, 0);
+    RPKV_EXP_PAIR(4);
+    RPKV_EXP_PAIR(5);
+    nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[3], qf[3], nxt, 0, 0, 0);
+    A.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[0][1], pb0, A.o1, 0, 0, 0);
+    RPKV_EXP_PAIR(6);
+    RPKV_EXP_PAIR(7);
+#undef RPKV_EXP_PAIR
+    const bf16x8 pb1 = __builtin_shufflevector(__builtin_shufflevector(pr[4], pr[5], 0, 1, 2, 3),
+                                               __builtin_shufflevector(pr[6], pr[7], 0, 1, 2, 3),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
+    A.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[1][0], pb1, A.o0, 0, 0, 0);
+    A.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[1][1], pb1, A.o1, 0, 0, 0);
+    // Keep this half's row sums here (not sunk past the barrier that may
+    // follow), so its weights die now.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(A.lp[e]));
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
@@ -259,27 +247,56 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
     const int h = rest % a.H;
     const int s = rest / a.H;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     const int hh = lane >> 5, col = lane & 31;
     const CacheState* st = a.states + s;
-    Walk w;
-    w.vis_n = st->vis_n;
-    w.vis_sp = st->vis_sp_tokens;
-    for (int i = tid; i < w.vis_n; i += 256) s_vis[i] = st->vis[i];
-    w.vis = s_vis;
-    w.tpp = a.tpp;
-    w.P = a.P;
-    w.slot_cap = a.slot_cap;
-    w.sp_cap = a.sp_cap;
-    const size_t head_pool = (size_t)h * a.pool * a.slot_cap * kHeadDim;
-    w.kbase = (const uint16_t*)a.kpool + s * a.kpool_elems + head_pool;
-    w.vbase = (const uint16_t*)a.vpool + s * a.kpool_elems + head_pool;
-    w.kspb = (const uint16_t*)a.ksp + s * a.ksp_elems + (size_t)h * a.sp_cap * kHeadDim;
-    w.vspb = (const uint16_t*)a.vsp + s * a.ksp_elems + (size_t)h * kHeadDim * a.sp_cap;
+    const int vis_n = uniform(st->vis_n);
+    const int vis_sp = uniform(st->vis_sp_tokens);
+    for (int i = tid; i < vis_n; i += 256) s_vis[i] = st->vis[i];
 
-    const int n_tiles = w.vis_n * a.tpp + (w.vis_sp + kTile - 1) / kTile;
-    const int t0 = (int)((long long)split * n_tiles / a.splits);
-    const int t1 = (int)((long long)(split + 1) * n_tiles / a.splits);
+    Loader ld;
+    {
+        const size_t head_bytes = (size_t)a.pool * a.slot_cap * kHeadDim * 2;
+        const size_t sp_bytes = (size_t)a.sp_cap * kHeadDim * 2;
+        const char* kp = a.kpool + (s * a.kpool_elems) * 2 + h * head_bytes;
+        const char* vp = a.vpool + (s * a.kpool_elems) * 2 + h * head_bytes;
+        const char* ks = a.ksp + (s * a.ksp_elems) * 2 + h * sp_bytes;
+        const char* vs = a.vsp + (s * a.ksp_elems) * 2 + h * sp_bytes;
+        ld.kpool = buffer_over(kp, head_bytes);
+        ld.vpool = buffer_over(vp, head_bytes);
+        ld.ksp = buffer_over(ks, sp_bytes);
+        ld.vsp = buffer_over(vs, sp_bytes);
+    }
+    ld.vis = s_vis;
+    ld.vis_n = vis_n;
+    ld.tpp = a.tpp;
+    ld.slot_cap = a.slot_cap;
+    // LDS tile layout: row r at r*128 bytes, its 16-byte chunk c stored at
+    // position c ^ ((r >> 1) & 7).  A 128-byte row spans half of the 64 LDS
+    // banks, so any 16 consecutive rows read at one logical chunk (the 16 lanes
+    // the LDS serves together) land on 16 distinct bank quads.
+    // Per-lane load offsets (row = 16*wave + 8*slab + lane/8).
+    {
+        uint32_t lk[2], lvp[2], lvs[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = (wave * 2 + i) * 8 + (lane >> 3);
+            const int ch = (lane & 7) ^ ((r >> 1) & 7);
+            lk[i] = r * 128 + ch * 16;
+            lvp[i] = r * a.slot_cap * 2 + ch * 16;
+            lvs[i] = r * a.sp_cap * 2 + ch * 16;
+        }
+        ld.lk0 = lk[0];
+        ld.lk1 = lk[1];
+        ld.lvp0 = lvp[0];
+        ld.lvp1 = lvp[1];
+        ld.lvs0 = lvs[0];
+        ld.lvs1 = lvs[1];
+    }
+    const int n_patch_tiles = vis_n * a.tpp;
+    const int n_tiles = n_patch_tiles + (vis_sp + kTile - 1) / kTile;
+    const int t0 = uniform((int)((long long)split * n_tiles / a.splits));
+    const int t1 = uniform((int)((long long)(split + 1) * n_tiles / a.splits));
     const int n = t1 - t0;
 
     // Q^T operands of this wave's 32 queries (B operand: column = query),
@@ -307,60 +324,72 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
     for (int i = 0; i < 16; ++i) {
         A.o0[i] = 0.f;
         A.o1[i] = 0.f;
-        A.negM[i] = 0.f;
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) A.lp[e] = 0.f;
     A.M = 0.f;
-    A.l = 0.f;
     A.first = true;
 
-    // LDS tile layout: row r at r*128 bytes, its 16-byte chunk c stored at
-    // position c ^ ((r >> 1) & 7).  A 128-byte row spans half of the 64 LDS
-    // banks, so any 16 consecutive rows read at one logical chunk (the 16 lanes
-    // the LDS serves together) land on 16 distinct bank quads.
-    // Per-lane load offsets (row = 16*wave + 8*slab + lane/8).
-    uint32_t lk[2], lvp[2], lvs[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r = (wave * 2 + i) * 8 + (lane >> 3);
-        const int ch = (lane & 7) ^ ((r >> 1) & 7);
-        lk[i] = (r * kHeadDim + ch * 8) * 2;
-        lvp[i] = (r * a.slot_cap + ch * 8) * 2;
-        lvs[i] = (r * a.sp_cap + ch * 8) * 2;
-    }
     // Operand byte offsets inside a tile ((row >> 1) & 7 == (col >> 1) & 7 for
-    // both 32-row blocks).
+    // every 32-row block).
     int foff[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) foff[j] = col * 128 + (((2 * j + hh) ^ ((col >> 1) & 7)) << 4);
 
     __syncthreads();   // s_vis ready
 
-    // Prologue: tiles 0 .. kStages-2 in flight.
-    Cursor ld = w.at(t0), cp = ld;
+    // Prologue: tiles 0 .. kStages-2 in flight; wait for tile 0.
 #pragma unroll
     for (int i = 0; i < kStages - 1; ++i)
-        if (i < n) {
-            w.issue(ld, lds + i * kStageBytes, wave, lk[0], lk[1], lvp[0], lvp[1], lvs[0], lvs[1]);
-            w.next(ld);
+        if (i < n) ld.issue(t0 + i, lds + i * kStageBytes, wave);
+    if (n >= kStages - 1)
+        wait_vmcnt<4 * (kStages - 2)>();
+    else if (n == 2)
+        wait_vmcnt<4>();
+    else
+        wait_vmcnt<0>();
+    __syncthreads();
+
+    // sA: first half of the tile being computed, sB: its second half.  The
+    // products of a half are formed one half ahead of its softmax; past the
+    // last tile they read a stale stage and are never used.
+    f32x16 sA = scores(lds, 0, foff, qf);
+    f32x16 sB;
+    // Tiles in groups of kStages, so every stage offset is a constant that
+    // folds into the LDS instructions' immediate offsets.  Past the last tile
+    // the next scores read a stale stage and are never used.
+    for (int i0 = 0; i0 < n; i0 += kStages) {
+#pragma unroll
+        for (int u = 0; u < kStages; ++u) {
+            const int i = i0 + u, t = t0 + i;
+            if (i >= n) break;
+            const char* cur = lds + u * kStageBytes;
+            const char* nxt = lds + ((u + 1) % kStages) * kStageBytes;
+            const int len = uniform(t < n_patch_tiles ? min(kTile, a.P - (t % a.tpp) * kTile)
+                                                      : min(kTile, vis_sp - (t - n_patch_tiles) * kTile));
+            step(sA, sB, cur, 0, len, cur + kHalfBytes, foff, qf, hh, A);
+            if (i + 1 < n) {
+                // Tile i+1 landed for every wave (later tiles may still be in
+                // flight), and every wave is done with tile i-1, whose stage
+                // now takes tile i+kStages-1.
+                if (kStages == 4 && i + 2 < n)
+                    wait_vmcnt<4>();
+                else
+                    wait_vmcnt<0>();
+                __syncthreads();
+                if (i + kStages - 1 < n)
+                    ld.issue(t + kStages - 1, lds + ((u + kStages - 1) % kStages) * kStageBytes, wave);
+            }
+            if (len > 32)
+                step(sB, sA, cur, 1, len, nxt, foff, qf, hh, A);
+            else
+                sA = scores(nxt, 0, foff, qf);
         }
-    Ctx x;
-    x.w = &w;
-    x.lds = lds;
-    x.qf = qf;
-    x.foff = foff;
-    x.wave = wave;
-    x.hh = hh;
-    x.n = n;
-    x.lk0 = lk[0];
-    x.lk1 = lk[1];
-    x.lvp0 = lvp[0];
-    x.lvp1 = lvp[1];
-    x.lvs0 = lvs[0];
-    x.lvs1 = lvs[1];
-    for (int i = 0; i < n; ++i) step(x, i, ld, cp, A);
+    }
 
     // Row sum over both half-waves; output O = O^T / l.
-    float l = A.l + __shfl_xor(A.l, 32);
+    float l = (A.lp[0] + A.lp[1]) + (A.lp[2] + A.lp[3]);
+    l += __shfl_xor(l, 32);
     const bool empty = !(l > 0.f);
     const float inv = empty ? 0.f : 1.f / l;
     const float lse_v = empty ? -INFINITY : (A.M + __log2f(l)) * 0.69314718055994531f;

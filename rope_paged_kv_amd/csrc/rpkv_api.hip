@@ -35,13 +35,29 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 // Picks the number of key-range splits of the bf16 attention: enough
 // workgroups to fill the chip about once (256 CUs x 4 resident workgroups),
 // without splits shorter than 8 key tiles at full cache occupancy.
+// Key-range splits of attend_frame.  The bf16 kernel keeps 3 workgroups
+// resident per compute unit (256 of them on MI355X), and a launch takes
+// ceil(workgroups / 768) rounds; splitting shortens each workgroup but adds a
+// round trip of fp32 partial outputs through the merge.  The estimate below
+// (in microseconds, from measured rates: ~1.36 us per 64-key tile per
+// workgroup at full residency, ~2 tiles of fixed cost per workgroup, partials
+// moved at ~4 TB/s) is taken at the largest visible set the cache can hold.
 int auto_splits(const Layout& L) {
-    const int base = L.q_tiles * L.H * L.S;
+    constexpr int kResident = 3 * 256;
+    const long long base = (long long)L.q_tiles * L.H * L.S;
     const int max_tiles = L.pool * L.tpp + (L.sp_cap + kTile - 1) / kTile;
-    int s = (1024 + base / 2) / base;
-    s = s < max_tiles / 8 ? s : max_tiles / 8;
-    s = s > 32 ? 32 : s;
-    return s < 1 ? 1 : s;
+    const double part_us = (double)L.S * L.H * L.N * 520.0 / 4.0e6;
+    int best = 1;
+    double best_us = 0.0;
+    for (int s = 1; s <= 32 && s <= max_tiles; ++s) {
+        const long long rounds = (base * s + kResident - 1) / kResident;
+        const double us = rounds * ((double)max_tiles / s + 2.0) * 1.36 + (s > 1 ? 3.0 + s * part_us : 0.0);
+        if (s == 1 || us < best_us) {
+            best = s;
+            best_us = us;
+        }
+    }
+    return best;
 }
 
 bool layout(const kv_config* c, Layout* L) {
@@ -85,6 +101,11 @@ bool layout(const kv_config* c, Layout* L) {
         l.splits = 1;
     else
         l.splits = c->attn_splits > 0 ? (c->attn_splits > 64 ? 64 : c->attn_splits) : auto_splits(l);
+    // The bf16 attention kernel addresses one head's pages through a 32-bit
+    // buffer offset.
+    if (c->dtype == RPKV_BF16 && ((size_t)l.pool * l.slot_cap * kHeadDim * 2 >= (1ull << 32) ||
+                                  (size_t)l.sp_cap * kHeadDim * 2 >= (1ull << 32)))
+        return false;
     l.state_bytes = round_up(sizeof(CacheState), 256);
     l.kpool_elems = (size_t)l.H * l.pool * l.slot_cap * kHeadDim;
     l.ksp_elems = (size_t)l.H * l.sp_cap * kHeadDim;
