@@ -72,28 +72,14 @@ struct Vec<float> {
     }
 };
 
-// Rotates the kCh/2 pairs of one chunk of Q and of K: pair j uses the t table
-// for j < pt, the h table for the next ph pairs and the w table after that.
-template <int kPairs>
-__device__ inline void rotate_pairs(float* fq, float* fk, int j0, const AppendArgs& a, int hp,
-                                    int wp) {
-#pragma unroll
-    for (int p = 0; p < kPairs; ++p) {
-        const int j = j0 + p;
-        float2 cs;
-        if (j < a.pt)
-            cs = a.tab_t[a.frame * a.pt + j];
-        else if (j < a.pt + a.ph)
-            cs = a.tab_h[hp * a.ph + (j - a.pt)];
-        else
-            cs = a.tab_w[wp * a.pw + (j - a.pt - a.ph)];
-        const float xq = fq[2 * p], yq = fq[2 * p + 1];
-        fq[2 * p] = xq * cs.x - yq * cs.y;
-        fq[2 * p + 1] = xq * cs.y + yq * cs.x;
-        const float xk = fk[2 * p], yk = fk[2 * p + 1];
-        fk[2 * p] = xk * cs.x - yk * cs.y;
-        fk[2 * p + 1] = xk * cs.y + yk * cs.x;
-    }
+// Rotation coefficients (cos, sin) of pair j of a token at grid position
+// (hp, wp): the t table for j < pt, the h table for the next ph pairs and the
+// w table after that.
+__device__ inline float2 coeff(const AppendArgs& a, int j, int hp, int wp) {
+    const float2* src = j < a.pt ? a.tab_t + a.frame * a.pt + j
+                      : j < a.pt + a.ph ? a.tab_h + hp * a.ph + (j - a.pt)
+                                        : a.tab_w + wp * a.pw + (j - a.pt - a.ph);
+    return *src;
 }
 
 template <typename T>
@@ -102,20 +88,10 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
     constexpr int CPR = kHeadDim / CH;     // chunks per row
     constexpr int NCH = kTile * CPR;       // chunks per tile and tensor
     constexpr int PER = NCH / 256;         // chunks per thread
-    __shared__ T vt[kTile][kHeadDim + CH];
+    __shared__ T vt[kHeadDim][kTile + CH]; // V^T of the tile: row d, storage position
 
     const int tile = blockIdx.x, h = blockIdx.y, s = blockIdx.z, tid = threadIdx.x;
     CacheState* st = a.states + s;
-
-    // Target of this append, from the state as it stands.
-    const int status = st->status;
-    const int n_free = st->n_free;
-    const int fresh = st->fresh;
-    const int page = n_free > 0 ? st->free_[n_free - 1] : fresh;
-    const int sp_off = st->n_sp;
-    // The special stream always has room for one frame beyond the committed
-    // ones; its capacity is checked when the frame is committed.
-    const bool ok = status == RPKV_OK && (n_free > 0 || fresh < a.pool);
 
     const bool special = tile == 0;
     const int slot0 = special ? 0 : (tile - 1) * kTile;
@@ -128,6 +104,45 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
     const T* kb = (const T*)a.k + in_off;
     const T* vb = (const T*)a.v + in_off;
     T* qrb = (T*)a.q_rot + in_off;
+
+    // Every load first, none waiting on another: this thread's chunks of Q,
+    // K and V (rows past the tile's tokens read row 0 and are dropped), then
+    // the rotation coefficients of its pairs.  The bookkeeping state, read
+    // next through the scalar cache, only decides where the results go.
+    uint4 qv[PER], kv[PER], vv[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int id = tid + i * 256;
+        const int r = id / CPR, c = id % CPR;
+        const size_t off = (size_t)(r < nrows ? r : 0) * rs + c * CH;
+        qv[i] = *(const uint4*)(qb + off);
+        kv[i] = *(const uint4*)(kb + off);
+        vv[i] = *(const uint4*)(vb + off);
+    }
+    float2 cs[PER][CH / 2];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int id = tid + i * 256;
+        const int r = id / CPR, c = id % CPR;
+        int hp = 0, wp = 0;   // specials sit at h = w = 0
+        if (!special) {
+            const int p = slot0 + (r < nrows ? r : 0);
+            hp = p / a.gw;
+            wp = p - hp * a.gw;
+        }
+#pragma unroll
+        for (int e = 0; e < CH / 2; ++e) cs[i][e] = coeff(a, c * (CH / 2) + e, hp, wp);
+    }
+
+    // Target of this append, from the state as it stands.
+    const int status = st->status;
+    const int n_free = st->n_free;
+    const int fresh = st->fresh;
+    const int page = n_free > 0 ? st->free_[n_free - 1] : fresh;
+    const int sp_off = st->n_sp;
+    // The special stream always has room for one frame beyond the committed
+    // ones; its capacity is checked when the frame is committed.
+    const bool ok = status == RPKV_OK && (n_free > 0 || fresh < a.pool);
     T* kdst;
     if (special)
         kdst = (T*)a.ksp + s * a.ksp_elems + ((size_t)h * a.sp_cap + sp_off) * kHeadDim;
@@ -135,32 +150,36 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
         kdst = (T*)a.kpool + s * a.kpool_elems +
                (((size_t)h * a.pool + page) * a.slot_cap + slot0) * kHeadDim;
 
+    // Rotate (a complex product per pair in fp32, rounded once), store Q and
+    // K; V goes to LDS transposed, at its storage position.
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int id = tid + i * 256;
         const int r = id / CPR, c = id % CPR;
         const bool valid = r < nrows;
-        uint4 qv = make_uint4(0, 0, 0, 0), kv = qv, vv = qv;
-        if (valid) {
-            qv = *(const uint4*)(qb + r * rs + c * CH);
-            kv = *(const uint4*)(kb + r * rs + c * CH);
-            vv = *(const uint4*)(vb + r * rs + c * CH);
-        }
-        int hp = 0, wp = 0;   // specials and rows past the tile sit at h = w = 0
-        if (!special && valid) {
-            const int p = slot0 + r;
-            hp = p / a.gw;
-            wp = p - hp * a.gw;
-        }
         float fq[CH], fk[CH];
-        Vec<T>::unpack(qv, fq);
-        Vec<T>::unpack(kv, fk);
-        rotate_pairs<CH / 2>(fq, fk, c * (CH / 2), a, hp, wp);
+        Vec<T>::unpack(qv[i], fq);
+        Vec<T>::unpack(kv[i], fk);
+#pragma unroll
+        for (int e = 0; e < CH / 2; ++e) {
+            const float2 w = cs[i][e];
+            const float xq = fq[2 * e], yq = fq[2 * e + 1];
+            fq[2 * e] = xq * w.x - yq * w.y;
+            fq[2 * e + 1] = xq * w.y + yq * w.x;
+            const float xk = fk[2 * e], yk = fk[2 * e + 1];
+            fk[2 * e] = xk * w.x - yk * w.y;
+            fk[2 * e + 1] = xk * w.y + yk * w.x;
+        }
         if (valid) {
             *(uint4*)(qrb + r * rs + c * CH) = Vec<T>::pack(fq);
             if (ok) *(uint4*)(kdst + r * kHeadDim + c * CH) = Vec<T>::pack(fk);
         }
-        *(uint4*)&vt[r][c * CH] = vv;   // zeros for rows past the tile's tokens
+        // Rows past the tile's tokens are zeros (padding slots stay zero).
+        const uint4 v = valid ? vv[i] : make_uint4(0, 0, 0, 0);
+        const T* ve = (const T*)&v;
+        const int pos = special ? r : vslot_perm(r);
+#pragma unroll
+        for (int e = 0; e < CH; ++e) vt[c * CH + e][pos] = ve[e];
     }
     __syncthreads();
 
@@ -173,19 +192,13 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
             for (int i = 0; i < PER; ++i) {
                 const int id = tid + i * 256;
                 const int d = id / CPR, g = id % CPR;
-                union {
-                    T t[CH];
-                    uint4 u;
-                } pk;
-#pragma unroll
-                for (int e = 0; e < CH; ++e) pk.t[e] = vt[vslot_perm(g * CH + e)][d];
-                *(uint4*)(vdst + (size_t)d * a.slot_cap + g * CH) = pk.u;
+                *(uint4*)(vdst + (size_t)d * a.slot_cap + g * CH) = *(const uint4*)&vt[d][g * CH];
             }
         } else {
             T* vdst = (T*)a.vsp + s * a.ksp_elems + (size_t)h * kHeadDim * a.sp_cap;
             for (int id = tid; id < a.nsp * kHeadDim; id += 256) {
                 const int r = id / kHeadDim, d = id % kHeadDim;
-                vdst[(size_t)d * a.sp_cap + vslot_perm(sp_off + r)] = vt[r][d];
+                vdst[(size_t)d * a.sp_cap + vslot_perm(sp_off + r)] = vt[d][r];
             }
         }
     }
