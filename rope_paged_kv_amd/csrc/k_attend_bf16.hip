@@ -16,9 +16,10 @@
 //    of P tokens is ceil(P/64) tiles; the special stream, whose pages are
 //    appended in order and never evicted, is contiguous per head);
 //  * tiles stream from HBM straight into LDS (buffer_load ... lds: no staging
-//    registers, the page offset in a scalar register) through a ring of
-//    stages, one barrier per tile; 16-byte chunks are XOR-swizzled so operand
-//    reads hit 64 distinct banks;
+//    registers, the page offset in a scalar register) through rings of 2 K
+//    and 3 V^T stages, one barrier per tile; 16-byte chunks are XOR-swizzled
+//    so operand reads hit 64 distinct banks; 40 KB of LDS and at most 128
+//    VGPRs let 4 workgroups (4 waves per SIMD) share a compute unit;
 //  * scores are formed transposed, S^T = K Q^T (keys on the MFMA rows, queries
 //    on the columns): each lane holds 16 scores of one query per 32-key half
 //    tile, so the softmax statistics stay in-lane but for one exchange with
@@ -45,19 +46,19 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-#ifndef RPKV_ATTN_STAGES
-#define RPKV_ATTN_STAGES 3
-#endif
 constexpr int kWaves = 4;
 constexpr int kQW = 32;                          // queries per wave
 constexpr int kQB = kWaves * kQW;                // queries per workgroup
-constexpr int kStages = RPKV_ATTN_STAGES;        // LDS ring; tile i+kStages-2 loads during tile i
 constexpr int kTileBytes = kTile * kHeadDim * 2; // one 64x64 bf16 tile: 8 KB
-constexpr int kStageBytes = 2 * kTileBytes;      // K tile + V^T tile
 constexpr int kHalfBytes = 32 * 128;             // 32 rows of a tile
+// LDS rings: K tiles in 2 stages, V^T tiles in 3.  K of tile i is read from
+// the barrier of tile i up to the barrier of tile i+1, V^T of tile i up to
+// the barrier of tile i+2; tile i+2 is loaded from the barrier of tile i+1.
+constexpr int kKStages = 2, kVStages = 3;
+constexpr int kGroup = 6;                        // tiles per unrolled group (lcm of the rings)
+constexpr int kLdsBytes = (kKStages + kVStages) * kTileBytes;
 // Word 3 of a raw (unstructured) buffer resource on gfx9: 32-bit data format.
 constexpr int kBufWord3 = 0x00020000;
-static_assert(kStages >= 3, "tile i is still read after the barrier of tile i+1");
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
 // 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
@@ -85,14 +86,15 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_over(const char* p, size_t bytes
 // swizzle).  All page arithmetic is scalar.
 struct Loader {
     __amdgpu_buffer_rsrc_t kpool, vpool, ksp, vsp;
-    const int* vis;          // visible pages (LDS copy)
+    const int* vis;          // visible pages (read through the scalar cache)
     int vis_n, tpp, slot_cap;
     uint32_t lk0, lk1, lvp0, lvp1, lvs0, lvs1;
 
     // Issues this wave's share of tile t (rows 16*wave .. 16*wave+15 of the K
     // tile and of the V^T tile, 8 rows per instruction) into an LDS stage.
-    __device__ void issue(int t, char* stage, int wave) const {
-        char* s0 = stage + wave * 2 * 8 * 128;
+    __device__ void issue(int t, char* kstage, char* vstage, int wave) const {
+        char* k0 = kstage + wave * 2 * 8 * 128;
+        char* v0 = vstage + wave * 2 * 8 * 128;
         const int npt = vis_n * tpp;
         if (t < npt) {
             const int pi = t / tpp;
@@ -100,19 +102,17 @@ struct Loader {
             const uint32_t page = (uint32_t)uniform(vis[pi]);
             const uint32_t ko = (page * (uint32_t)slot_cap + off) * 128u;
             const uint32_t vo = page * (uint32_t)slot_cap * 128u + off * 2u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kpool, (lds_void_ptr)s0, 16, lk0, ko, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kpool, (lds_void_ptr)(s0 + 1024), 16, lk1, ko, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vpool, (lds_void_ptr)(s0 + kTileBytes), 16, lvp0, vo, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vpool, (lds_void_ptr)(s0 + kTileBytes + 1024), 16, lvp1, vo,
-                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kpool, (lds_void_ptr)k0, 16, lk0, ko, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kpool, (lds_void_ptr)(k0 + 1024), 16, lk1, ko, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vpool, (lds_void_ptr)v0, 16, lvp0, vo, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vpool, (lds_void_ptr)(v0 + 1024), 16, lvp1, vo, 0, 0);
         } else {
             const uint32_t off = (uint32_t)(t - npt) * kTile;
             const uint32_t ko = off * 128u, vo = off * 2u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksp, (lds_void_ptr)s0, 16, lk0, ko, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksp, (lds_void_ptr)(s0 + 1024), 16, lk1, ko, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vsp, (lds_void_ptr)(s0 + kTileBytes), 16, lvs0, vo, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vsp, (lds_void_ptr)(s0 + kTileBytes + 1024), 16, lvs1, vo, 0,
-                                                     0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksp, (lds_void_ptr)k0, 16, lk0, ko, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksp, (lds_void_ptr)(k0 + 1024), 16, lk1, ko, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vsp, (lds_void_ptr)v0, 16, lvs0, vo, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vsp, (lds_void_ptr)(v0 + 1024), 16, lvs1, vo, 0, 0);
         }
     }
 };
@@ -147,7 +147,7 @@ __device__ __forceinline__ f32x16 scores(const char* tile, int kb, const int* fo
 // tile into nxt (K rows at knext; the caller makes sure they are loaded, or
 // ignores nxt).  Key of sc[r]: 32*kb + 8*(r/4) + 4*hh + r%4; its V^T column
 // sits at that key's slot, chunk 4*kb + 2*(r/8) + hh.
-__device__ __forceinline__ void step(f32x16& sc, f32x16& nxt, const char* tile, int kb, int len,
+__device__ __forceinline__ void step(f32x16& sc, f32x16& nxt, const char* vt, int kb, int len,
                                      const char* knext, const int* foff, const bf16x8* qf, int hh,
                                      Acc& A) {
     if (len < 32 * kb + 32) {   // ragged: keys past the tile's end do not count
@@ -179,7 +179,6 @@ __device__ __forceinline__ void step(f32x16& sc, f32x16& nxt, const char* tile, 
         }
     }
     // LDS operands: V^T fragments of this half, K fragments of the next.
-    const char* vt = tile + kTileBytes;
     bf16x8 v[2][2], k[4];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -230,9 +229,10 @@ __device__ __forceinline__ void step(f32x16& sc, f32x16& nxt, const char* tile, 
     __builtin_amdgcn_sched_barrier(0);
 }
 
-__global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
-    __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes];
-    __shared__ int s_vis[kMaxPool];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_attend_bf16(AttnArgs a) {
+    __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+    char* const kring = lds;
+    char* const vring = lds + kKStages * kTileBytes;
 
     // Logical workgroup id: consecutive physical ids go round-robin to the 8
     // XCDs, so the remap gives each XCD a contiguous range of logical ids; the
@@ -252,7 +252,6 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
     const CacheState* st = a.states + s;
     const int vis_n = uniform(st->vis_n);
     const int vis_sp = uniform(st->vis_sp_tokens);
-    for (int i = tid; i < vis_n; i += 256) s_vis[i] = st->vis[i];
 
     Loader ld;
     {
@@ -267,7 +266,7 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
         ld.ksp = buffer_over(ks, sp_bytes);
         ld.vsp = buffer_over(vs, sp_bytes);
     }
-    ld.vis = s_vis;
+    ld.vis = st->vis;
     ld.vis_n = vis_n;
     ld.tpp = a.tpp;
     ld.slot_cap = a.slot_cap;
@@ -336,15 +335,10 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) foff[j] = col * 128 + (((2 * j + hh) ^ ((col >> 1) & 7)) << 4);
 
-    __syncthreads();   // s_vis ready
-
-    // Prologue: tiles 0 .. kStages-2 in flight; wait for tile 0.
-#pragma unroll
-    for (int i = 0; i < kStages - 1; ++i)
-        if (i < n) ld.issue(t0 + i, lds + i * kStageBytes, wave);
-    if (n >= kStages - 1)
-        wait_vmcnt<4 * (kStages - 2)>();
-    else if (n == 2)
+    // Prologue: tiles 0 and 1 in flight; wait for tile 0.
+    if (n > 0) ld.issue(t0, kring, vring, wave);
+    if (n > 1) ld.issue(t0 + 1, kring + kTileBytes, vring + kTileBytes, wave);
+    if (n > 1)
         wait_vmcnt<4>();
     else
         wait_vmcnt<0>();
@@ -353,37 +347,34 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
     // sA: first half of the tile being computed, sB: its second half.  The
     // products of a half are formed one half ahead of its softmax; past the
     // last tile they read a stale stage and are never used.
-    f32x16 sA = scores(lds, 0, foff, qf);
+    f32x16 sA = scores(kring, 0, foff, qf);
     f32x16 sB;
-    // Tiles in groups of kStages, so every stage offset is a constant that
-    // folds into the LDS instructions' immediate offsets.  Past the last tile
-    // the next scores read a stale stage and are never used.
-    for (int i0 = 0; i0 < n; i0 += kStages) {
+    // Tiles in groups of kGroup, so every stage offset is a constant that
+    // folds into the LDS instructions' immediate offsets.
+    for (int i0 = 0; i0 < n; i0 += kGroup) {
 #pragma unroll
-        for (int u = 0; u < kStages; ++u) {
+        for (int u = 0; u < kGroup; ++u) {
             const int i = i0 + u, t = t0 + i;
             if (i >= n) break;
-            const char* cur = lds + u * kStageBytes;
-            const char* nxt = lds + ((u + 1) % kStages) * kStageBytes;
+            const char* kcur = kring + (u % kKStages) * kTileBytes;
+            const char* knxt = kring + ((u + 1) % kKStages) * kTileBytes;
+            const char* vcur = vring + (u % kVStages) * kTileBytes;
             const int len = uniform(t < n_patch_tiles ? min(kTile, a.P - (t % a.tpp) * kTile)
                                                       : min(kTile, vis_sp - (t - n_patch_tiles) * kTile));
-            step(sA, sB, cur, 0, len, cur + kHalfBytes, foff, qf, hh, A);
+            step(sA, sB, vcur, 0, len, kcur + kHalfBytes, foff, qf, hh, A);
             if (i + 1 < n) {
-                // Tile i+1 landed for every wave (later tiles may still be in
-                // flight), and every wave is done with tile i-1, whose stage
-                // now takes tile i+kStages-1.
-                if (kStages == 4 && i + 2 < n)
-                    wait_vmcnt<4>();
-                else
-                    wait_vmcnt<0>();
+                // Tile i+1 landed for every wave, every wave is done with K of
+                // tile i and V^T of tile i-1: their stages take tile i+2.
+                wait_vmcnt<0>();
                 __syncthreads();
-                if (i + kStages - 1 < n)
-                    ld.issue(t + kStages - 1, lds + ((u + kStages - 1) % kStages) * kStageBytes, wave);
+                if (i + 2 < n)
+                    ld.issue(t + 2, kring + ((u + 2) % kKStages) * kTileBytes,
+                             vring + ((u + 2) % kVStages) * kTileBytes, wave);
             }
             if (len > 32)
-                step(sB, sA, cur, 1, len, nxt, foff, qf, hh, A);
+                step(sB, sA, vcur, 1, len, knxt, foff, qf, hh, A);
             else
-                sA = scores(nxt, 0, foff, qf);
+                sA = scores(knxt, 0, foff, qf);
         }
     }
 

@@ -35,23 +35,26 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 // Picks the number of key-range splits of the bf16 attention: enough
 // workgroups to fill the chip about once (256 CUs x 4 resident workgroups),
 // without splits shorter than 8 key tiles at full cache occupancy.
-// Key-range splits of attend_frame.  The bf16 kernel keeps 3 workgroups
-// resident per compute unit (256 of them on MI355X), and a launch takes
-// ceil(workgroups / 768) rounds; splitting shortens each workgroup but adds a
-// round trip of fp32 partial outputs through the merge.  The estimate below
-// (in microseconds, from measured rates: ~1.36 us per 64-key tile per
-// workgroup at full residency, ~2 tiles of fixed cost per workgroup, partials
-// moved at ~4 TB/s) is taken at the largest visible set the cache can hold.
+// Key-range splits of attend_frame.  The bf16 kernel is bound by what each
+// compute unit (256 on MI355X) issues, so a launch lasts about as long as
+// the most loaded unit needs for its ceil(workgroups / 256) workgroups, and
+// with fewer than 2 workgroups per unit it runs ~1.5x slower per workgroup;
+// splitting shortens each workgroup but adds a round trip of fp32 partial
+// outputs through the merge.  The estimate (microseconds, from measured
+// rates: ~0.55 us per 64-key tile of a workgroup on a busy unit, ~2 tiles of
+// fixed cost per workgroup, partials moved at ~4 TB/s, ~3 us per merge
+// launch) is taken at the largest visible set the cache can hold.
 int auto_splits(const Layout& L) {
-    constexpr int kResident = 3 * 256;
+    constexpr int kCUs = 256;
     const long long base = (long long)L.q_tiles * L.H * L.S;
     const int max_tiles = L.pool * L.tpp + (L.sp_cap + kTile - 1) / kTile;
     const double part_us = (double)L.S * L.H * L.N * 520.0 / 4.0e6;
     int best = 1;
     double best_us = 0.0;
     for (int s = 1; s <= 32 && s <= max_tiles; ++s) {
-        const long long rounds = (base * s + kResident - 1) / kResident;
-        const double us = rounds * ((double)max_tiles / s + 2.0) * 1.36 + (s > 1 ? 3.0 + s * part_us : 0.0);
+        const long long wg = base * s;
+        const double busy = (double)((wg + kCUs - 1) / kCUs) * ((double)max_tiles / s + 2.0) * 0.552;
+        const double us = busy * (wg < 2 * kCUs ? 1.5 : 1.0) + (s > 1 ? 3.0 + s * part_us : 0.0);
         if (s == 1 || us < best_us) {
             best = s;
             best_us = us;
