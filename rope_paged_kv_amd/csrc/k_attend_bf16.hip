@@ -18,8 +18,7 @@
 //  * tiles stream from HBM straight into LDS (buffer_load ... lds: no staging
 //    registers, the page offset in a scalar register) through rings of 2 K
 //    and 3 V^T stages, one barrier per tile; 16-byte chunks are XOR-swizzled
-//    so operand reads hit 64 distinct banks; 40 KB of LDS and at most 128
-//    VGPRs let 4 workgroups (4 waves per SIMD) share a compute unit;
+//    so operand reads hit 64 distinct banks (40 KB of LDS per workgroup);
 //  * scores are formed transposed, S^T = K Q^T (keys on the MFMA rows, queries
 //    on the columns): each lane holds 16 scores of one query per 32-key half
 //    tile, so the softmax statistics stay in-lane but for one exchange with
@@ -31,10 +30,11 @@
 //    matrix core and the vector ALU work side by side (the next half of the
 //    last half tile of tile i is the first half of tile i+1, formed after the
 //    barrier of tile i+1);
-//  * Q is pre-multiplied by log2(e)/sqrt(D) and the score accumulators start
-//    at -M (the running reference max), so a product is already the base-2
-//    exponent and p = exp2(t) costs one transcendental; M moves (and the
-//    accumulated output is rescaled) only when a score exceeds it by 2^8;
+//  * scores s = q.k come out of the matrix core in fp32 from the stored bf16
+//    Q and K (no extra rounding of Q); one fused multiply-add per score turns
+//    s into the base-2 exponent t = s*log2(e)/sqrt(D) - M (M: the running
+//    reference max), and p = exp2(t) costs one transcendental; M moves (and
+//    the accumulated output is rescaled) only when a score exceeds it by 2^8;
 //  * several splits of the key range are merged by their log-sum-exp.
 #include "rpkv_internal.h"
 
@@ -121,11 +121,12 @@ struct Loader {
 struct Acc {
     f32x16 o0, o1;     // O^T, d rows 0-31 and 32-63
     float lp[4];       // partial row sums
-    float M;           // reference max of the base-2 scores
+    float M;           // reference max of the base-2 exponents
+    float c;           // log2(e)/sqrt(D)
     bool first;
 };
 
-// s = c*q.k for the 32 keys of half kb of a tile (rows 32*kb + col of the K
+// s = q.k for the 32 keys of half kb of a tile (rows 32*kb + col of the K
 // tile; chunk 2*j + hh is k-step j).
 __device__ __forceinline__ f32x16 scores(const char* tile, int kb, const int* foff, const bf16x8* qf) {
     const char* t = tile + kb * kHalfBytes;
@@ -162,10 +163,10 @@ __device__ __forceinline__ void step(f32x16& sc, f32x16& nxt, const char* vt, in
     const float md = max3f(sc[9], sc[10], sc[11]);
     const float me = max3f(sc[12], sc[13], sc[14]);
     const float mx = max3f(max3f(ma, mb, mc), fmaxf(md, me), sc[15]);
-    if (A.first || __any(mx > A.M + 8.f)) {
+    if (A.first || __any(fmaf(mx, A.c, -A.M) > 8.f)) {
         // rare: move M (jointly for both lanes of a query; never down after
         // the first half tile) and rescale what was accumulated.
-        const float d = fmaxf(mx, __shfl_xor(mx, 32));
+        const float d = fmaxf(mx, __shfl_xor(mx, 32)) * A.c;
         const float m_new = A.first ? d : fmaxf(d, A.M);
         const float alpha = A.first ? 0.f : __builtin_amdgcn_exp2f(A.M - m_new);
         A.first = false;
@@ -192,10 +193,11 @@ __device__ __forceinline__ void step(f32x16& sc, f32x16& nxt, const char* vt, in
     // up the matrix core).
     bf16x2 pr[8];
     const f32x16 zero = {};
+    const float nm = -A.M;
 #define RPKV_EXP_PAIR(e)                                                                           \
     do {                                                                                           \
-        const f32x2 x_ = {__builtin_amdgcn_exp2f(sc[2 * (e)] - A.M),                               \
-                          __builtin_amdgcn_exp2f(sc[2 * (e) + 1] - A.M)};                          \
+        const f32x2 x_ = {__builtin_amdgcn_exp2f(fmaf(sc[2 * (e)], A.c, nm)),                      \
+                          __builtin_amdgcn_exp2f(fmaf(sc[2 * (e) + 1], A.c, nm))};                 \
         pr[e] = __builtin_convertvector(x_, bf16x2);                                               \
         A.lp[(e) & 3] += x_[0] + x_[1];                                                            \
     } while (0)
@@ -229,7 +231,7 @@ __device__ __forceinline__ void step(f32x16& sc, f32x16& nxt, const char* vt, in
     __builtin_amdgcn_sched_barrier(0);
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_attend_bf16(AttnArgs a) {
+__global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
     char* const kring = lds;
     char* const vring = lds + kKStages * kTileBytes;
@@ -298,9 +300,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const int t1 = uniform((int)((long long)(split + 1) * n_tiles / a.splits));
     const int n = t1 - t0;
 
-    // Q^T operands of this wave's 32 queries (B operand: column = query),
-    // pre-multiplied by c = log2(e)/sqrt(D) and rounded once to bf16.
-    const float c = a.scale_log2;
+    // Q^T operands of this wave's 32 queries (B operand: column = query): the
+    // stored bf16 values as they are.
     const int q = qt * kQB + wave * kQW + col;
     const bool qvalid = q < a.N;
     bf16x8 qf[4];
@@ -309,12 +310,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 #pragma unroll
         for (int dc = 0; dc < 4; ++dc) {
             const uint4 u = qvalid ? *(const uint4*)(qp + dc * 16 + 8 * hh) : make_uint4(0, 0, 0, 0);
-            const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                qf[dc][2 * i] = (__bf16)(__uint_as_float(wv[i] << 16) * c);
-                qf[dc][2 * i + 1] = (__bf16)(__uint_as_float(wv[i] & 0xFFFF0000u) * c);
-            }
+            qf[dc] = __builtin_bit_cast(bf16x8, u);
         }
     }
 
@@ -327,6 +323,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 #pragma unroll
     for (int e = 0; e < 4; ++e) A.lp[e] = 0.f;
     A.M = 0.f;
+    A.c = a.scale_log2;
     A.first = true;
 
     // Operand byte offsets inside a tile ((row >> 1) & 7 == (col >> 1) & 7 for

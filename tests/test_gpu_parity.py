@@ -14,7 +14,7 @@ import rope_paged_kv_amd as rp
 from gpu_harness import Runner, make_cache, to_dev, torch_dtype
 from oracle import pages, rope3d
 from oracle.stream import OracleStream
-from rpkv_inputs import WORKLOADS, frame_qkv, qkv, small_variants
+from rpkv_inputs import WORKLOADS, frame_qkv, qkv, round_to_bf16, small_variants
 
 pytestmark = pytest.mark.gpu
 
@@ -269,6 +269,60 @@ def test_single_layer_37x37_sampled():
     frames = {0, 1, 7, 8, 23, 24, 25, 40, 63}
     worst, worst_lse = run_and_compare(wl, frames, rows=sampled_rows(wl))
     print(f"37x37 single layer: max|out-oracle| {worst:.3e}  max|lse-oracle| {worst_lse:.3e}")
+
+
+def test_attention_large_logits_move_the_reference_max():
+    """Peaked softmax: Q scaled by 3 and the keys of frame f by 1 + f/2, so
+    the scores span hundreds of base-2 units and later pages beat the running
+    max of earlier ones by more than 2^8 thousands of times.
+
+    The kernel rotates K in fp32 and the oracle exactly, both rounding to
+    bf16, so a rotated key element can differ by one bf16 ulp (checked
+    below: never more, and rarely).  Such a difference moves a score by
+    |q_d| * ulp, about 3 * 2^-5 = 0.1 (0.012 in natural-log units of the
+    scaled score): the LSE is therefore held to 5e-2 here, the outputs to
+    the usual 2e-2."""
+    wl = small_variants()["small_bf16"]
+
+    def gen(f, t):
+        x = qkv(wl, 0, 0, f, t)
+        if t == 0:
+            x = x * 3.0
+        elif t == 1:
+            x = x * (1.0 + 0.5 * f)
+        return round_to_bf16(x)
+
+    cache = make_cache(wl)
+    run = Runner(wl, cache)
+    orc = OracleStream(wl, lambda f, t: gen(f, t))
+    sim = sim_for(wl)
+    worst, worst_lse, flips, total = 0.0, 0.0, 0, 0
+    for f in range(wl.frames):
+        q, k, v = (to_dev(gen(f, t)[None], run.dt) for t in range(3))
+        commit = wl.is_keyframe(f)
+        run.cache.append(0, f, int(commit), q, k, v, run.q_rot)
+        sim.append(f, commit)
+        # rotated K of the frame's patches in its page: within one bf16 ulp
+        kp = _pages_for(cache, 0, 0)[0]
+        got_k = kp[:, sim.target, :wl.patches].float().cpu().numpy().transpose(1, 0, 2)
+        want_k = rope3d.round_bf16(orc.rotate(gen(f, 1), f))[wl.n_special:]
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(want_k), 1e-30))) - 7)
+        d = np.abs(got_k - want_k)
+        assert np.all(d <= ulp), f
+        flips += int((d > 0).sum())
+        total += d.size
+        run.cache.attend(0, run.q_rot, run.out, run.lse)
+        o, lse = orc.attend(f)
+        err = np.abs(run.out[0].float().cpu().numpy() - o).max()
+        lerr = np.abs(run.lse[0].cpu().numpy() - lse).max()
+        worst, worst_lse = max(worst, err), max(worst_lse, lerr)
+        assert err <= BF16_TOL, (f, err)
+        assert lerr <= 5e-2, (f, lerr)
+        sim.evict()
+        run.cache.evict(0)
+    assert flips <= 1e-3 * total, (flips, total)
+    print(f"large logits: max|out-oracle| {worst:.3e}  max|lse-oracle| {worst_lse:.3e}  "
+          f"K elements one ulp off: {flips}/{total}")
 
 
 def test_visibility_probe_q_zero():
