@@ -180,7 +180,7 @@ def bench_single_layer(wl, args, dev):
                            for x in stream_qkv(wl, 0, threads=min(16, os.cpu_count() or 1)))
     torch.cuda.synchronize()
     spec = rp.make_spec(pairs=wl.pairs, theta=wl.theta, ntk_factor=wl.ntk_factor,
-                        max_frames=wl.t_rows, max_h=wl.grid_h, max_w=wl.grid_w)
+                        max_frames=wl.t_rows, max_h=wl.grid_h, max_w=wl.grid_w, layout=wl.rope_layout)
     cfg = rp.make_config(num_layers=1, num_streams=wl.streams, num_heads=wl.heads,
                          grid_h=wl.grid_h, grid_w=wl.grid_w, dtype=wl.dtype,
                          patch_page_size=wl.page_size, special_page_size=wl.special_page_size,

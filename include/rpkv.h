@@ -83,13 +83,27 @@ enum { RPKV_BF16 = 0, RPKV_F32 = 1 };
  * The tables are sized from the grid (token counts), not from data, so no
  * device value is ever read back ([LONG] "Deriving Size from Token Count").
  */
+/* Channel layout of the rotation (rope3d_spec.layout):
+ *  - RPKV_ROPE_INTERLEAVED: pair j is channels (2j, 2j+1); the t axis takes
+ *    pairs 0..pairs_t-1, then h, then w ([ROPE-KV] "Complex-Valued Tensor
+ *    Application": a complex table of head_dim/2 entries per token);
+ *  - RPKV_ROPE_HALF_SPLIT: axis a owns a block of 2*pairs_a consecutive
+ *    channels (t, then h, then w) and pair i of that block is channels
+ *    (b + i, b + i + pairs_a): the block is split in halves, the 2D module's
+ *    arrangement ([LONG] "Understanding the 2D RoPE Architecture": vertical
+ *    and horizontal halves, base frequency 100).  Every pairs_a must be a
+ *    multiple of 8 here (whole 16-byte chunks per half). */
+#define RPKV_ROPE_INTERLEAVED 0
+#define RPKV_ROPE_HALF_SPLIT 1
+
 typedef struct {
     int head_dim;       /* D, even; pairs_t + pairs_h + pairs_w == D/2 */
     int pairs_t, pairs_h, pairs_w;
-    double theta;       /* base, e.g. 10000 */
+    double theta;       /* base, e.g. 10000 (100 for the 2D module) */
     double ntk_factor;  /* multiplies theta; 1 = none */
     int max_frames;     /* rows of the t table: frame indices 0..max_frames-1 */
     int max_h, max_w;   /* rows of the h and w tables (>= grid_h, grid_w) */
+    int layout;         /* RPKV_ROPE_INTERLEAVED or RPKV_ROPE_HALF_SPLIT */
 } rope3d_spec;
 
 /* Bytes of the rotary tables for `spec`; 0 if the spec is invalid. */

@@ -48,7 +48,7 @@ class OracleChain:
     def _rotate(self, x, frame):
         wl = self.wl
         return rope3d.rotate_frame(x, frame, wl.grid_h, wl.grid_w, wl.n_special, wl.pairs,
-                                   wl.theta, wl.ntk_factor)
+                                   wl.theta, wl.ntk_factor, layout=wl.rope_layout)
 
     def frame(self, f: int):
         """Run frame f through every layer. Returns (list of O_l [N, H, D], x_L [N, hidden])."""

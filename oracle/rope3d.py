@@ -24,6 +24,15 @@ KV-Cache Streaming"):
 
 Only Q and K are rotated; V is stored as is (page "How 3D RoPE ...", FAQ "Where
 does the RoPE application occur relative to the KV cache write?").
+
+Second channel layout, half-split (page "How to Handle Sequences Exceeding the
+RoPE Training Range in LingBot-Map", sections "Understanding the 2D RoPE
+Architecture" and "Spatial Position Encoding"): the 2D module gives the
+vertical and the horizontal axis one half of the features each and rotates
+each half on its own; reading: axis a owns a block of 2*pairs_a consecutive
+channels (t, h, w in that order) and pair i of the block is (block[i],
+block[i + pairs_a]), turned by the same angle pos * omega_{a,i} as above; the
+module's base frequency is 100 (the example's `frequency=100.0`).
 """
 from __future__ import annotations
 
@@ -77,10 +86,35 @@ def apply_rotary(x: np.ndarray, table: np.ndarray) -> np.ndarray:
     return out
 
 
+def apply_half_split(x: np.ndarray, table: np.ndarray, pairs=(12, 10, 10)) -> np.ndarray:
+    """Rotate x [N, H, D] (real) by the complex table [N, D/2] with the
+    half-split pairing: in the block of axis a, channel i and channel
+    i + pairs_a form the complex number block[i] + i*block[i + pairs_a]."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.float64)
+    ch = 0   # first channel of the axis block
+    col = 0  # first table column of the axis
+    for n_pairs in pairs:
+        re = x[..., ch:ch + n_pairs]
+        im = x[..., ch + n_pairs:ch + 2 * n_pairs]
+        z = (re + 1j * im) * table[:, None, col:col + n_pairs]
+        out[..., ch:ch + n_pairs] = z.real
+        out[..., ch + n_pairs:ch + 2 * n_pairs] = z.imag
+        ch += 2 * n_pairs
+        col += n_pairs
+    return out
+
+
+INTERLEAVED, HALF_SPLIT = 0, 1
+
+
 def rotate_frame(x: np.ndarray, frame: int, grid_h: int, grid_w: int, n_special: int = 6,
-                 pairs=(12, 10, 10), theta: float = 10000.0, ntk_factor: float = 1.0) -> np.ndarray:
+                 pairs=(12, 10, 10), theta: float = 10000.0, ntk_factor: float = 1.0,
+                 layout: int = INTERLEAVED) -> np.ndarray:
     """Rotate one frame's Q or K [N, H, D] at its (t, h, w) token positions."""
     tab = rotation_table(token_positions(frame, grid_h, grid_w, n_special), pairs, theta, ntk_factor)
+    if layout == HALF_SPLIT:
+        return apply_half_split(x, tab, pairs)
     return apply_rotary(x, tab)
 
 

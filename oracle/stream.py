@@ -34,7 +34,7 @@ class OracleStream:
     def rotate(self, x: np.ndarray, frame: int) -> np.ndarray:
         wl = self.wl
         return rope3d.rotate_frame(x, frame, wl.grid_h, wl.grid_w, wl.n_special, wl.pairs,
-                                   wl.theta, wl.ntk_factor)
+                                   wl.theta, wl.ntk_factor, layout=wl.rope_layout)
 
     def q_rot(self, frame: int) -> np.ndarray:
         """Rotated Q of the frame as stored for attention [N, H, D] (float64)."""

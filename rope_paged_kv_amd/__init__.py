@@ -107,10 +107,14 @@ def rpkv_strerror(code: int) -> str:
 
 # ---- convenience: device memory from torch --------------------------------
 
+ROPE_INTERLEAVED = 0
+ROPE_HALF_SPLIT = 1
+
+
 def make_spec(head_dim=64, pairs=(12, 10, 10), theta=10000.0, ntk_factor=1.0, max_frames=1,
-              max_h=1, max_w=1) -> Rope3dSpec:
+              max_h=1, max_w=1, layout=ROPE_INTERLEAVED) -> Rope3dSpec:
     return Rope3dSpec(head_dim, pairs[0], pairs[1], pairs[2], theta, ntk_factor, max_frames,
-                      max_h, max_w)
+                      max_h, max_w, layout)
 
 
 def make_config(*, num_layers, num_streams, num_heads, grid_h, grid_w, dtype="bf16", head_dim=64,

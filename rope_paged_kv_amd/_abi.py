@@ -18,7 +18,8 @@ EXPORTS = ("rope3d_tables_bytes", "rope3d_build_tables", "kv_required_bytes", "k
 class Rope3dSpec(C.Structure):
     _fields_ = [("head_dim", C.c_int), ("pairs_t", C.c_int), ("pairs_h", C.c_int),
                 ("pairs_w", C.c_int), ("theta", C.c_double), ("ntk_factor", C.c_double),
-                ("max_frames", C.c_int), ("max_h", C.c_int), ("max_w", C.c_int)]
+                ("max_frames", C.c_int), ("max_h", C.c_int), ("max_w", C.c_int),
+                ("layout", C.c_int)]
 
 
 class KvConfig(C.Structure):

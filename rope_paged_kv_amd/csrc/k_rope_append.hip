@@ -82,6 +82,52 @@ __device__ inline float2 coeff(const AppendArgs& a, int j, int hp, int wp) {
     return *src;
 }
 
+// Row and 16-byte chunk of a thread's chunk slot i.  Interleaved layout:
+// slots walk the tile's chunks in order.  Half-split layout: slots 2j and
+// 2j+1 are a pair of chunks that rotate together -- a chunk of the first half
+// of an axis block and the chunk pairs_a channels after it -- and the pair
+// slots walk the tile's first-half chunks in order (cpr/2 per row).
+template <int CH>
+__device__ inline void chunk_of(const AppendArgs& a, int tid, int i, int& r, int& c) {
+    constexpr int CPR = kHeadDim / CH;
+    if (a.layout == RPKV_ROPE_INTERLEAVED) {
+        const int id = tid + i * 256;
+        r = id / CPR;
+        c = id % CPR;
+        return;
+    }
+    const int id = tid + (i >> 1) * 256;
+    r = id / (CPR / 2);
+    int pc = id % (CPR / 2);
+    const int nt = a.pt / CH, nh = a.ph / CH, nw = a.pw / CH;   // first-half chunks per axis
+    int base, half;
+    if (pc < nt) {
+        base = 0;
+        half = nt;
+    } else if ((pc -= nt) < nh) {
+        base = 2 * nt;
+        half = nh;
+    } else {
+        pc -= nh;
+        base = 2 * (nt + nh);
+        half = nw;
+    }
+    c = base + pc + ((i & 1) ? half : 0);
+}
+
+// Rotation coefficients of a thread's chunk slots, flat: interleaved, pair e
+// of slot i at [i*CH/2 + e]; half-split, channel e of pair slot j at [j*CH + e].
+template <int CH>
+__device__ inline float2 coeff_of(const AppendArgs& a, int c, int e, int hp, int wp) {
+    if (a.layout == RPKV_ROPE_INTERLEAVED) return coeff(a, c * (CH / 2) + e, hp, wp);
+    // half-split: chunk c of the first half of its axis block; pair index
+    // inside the axis = channel offset from the block start.
+    const int nt = a.pt / CH, nh = a.ph / CH;
+    if (c < 2 * nt) return a.tab_t[a.frame * a.pt + c * CH + e];
+    if (c < 2 * (nt + nh)) return a.tab_h[hp * a.ph + (c - 2 * nt) * CH + e];
+    return a.tab_w[wp * a.pw + (c - 2 * (nt + nh)) * CH + e];
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
     constexpr int CH = Vec<T>::kCh;        // elements per 16-byte chunk
@@ -112,26 +158,31 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
     uint4 qv[PER], kv[PER], vv[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int id = tid + i * 256;
-        const int r = id / CPR, c = id % CPR;
+        int r, c;
+        chunk_of<CH>(a, tid, i, r, c);
         const size_t off = (size_t)(r < nrows ? r : 0) * rs + c * CH;
         qv[i] = *(const uint4*)(qb + off);
         kv[i] = *(const uint4*)(kb + off);
         vv[i] = *(const uint4*)(vb + off);
     }
-    float2 cs[PER][CH / 2];
+    float2 cs[PER * CH / 2];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int id = tid + i * 256;
-        const int r = id / CPR, c = id % CPR;
+        int r, c;
+        chunk_of<CH>(a, tid, i, r, c);
         int hp = 0, wp = 0;   // specials sit at h = w = 0
         if (!special) {
             const int p = slot0 + (r < nrows ? r : 0);
             hp = p / a.gw;
             wp = p - hp * a.gw;
         }
+        if (a.layout == RPKV_ROPE_INTERLEAVED) {
 #pragma unroll
-        for (int e = 0; e < CH / 2; ++e) cs[i][e] = coeff(a, c * (CH / 2) + e, hp, wp);
+            for (int e = 0; e < CH / 2; ++e) cs[i * (CH / 2) + e] = coeff_of<CH>(a, c, e, hp, wp);
+        } else if ((i & 1) == 0) {
+#pragma unroll
+            for (int e = 0; e < CH; ++e) cs[(i >> 1) * CH + e] = coeff_of<CH>(a, c, e, hp, wp);
+        }
     }
 
     // Target of this append, from the state as it stands.
@@ -152,27 +203,47 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
 
     // Rotate (a complex product per pair in fp32, rounded once), store Q and
     // K; V goes to LDS transposed, at its storage position.
+    float fq[PER][CH], fk[PER][CH];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int id = tid + i * 256;
-        const int r = id / CPR, c = id % CPR;
-        const bool valid = r < nrows;
-        float fq[CH], fk[CH];
-        Vec<T>::unpack(qv[i], fq);
-        Vec<T>::unpack(kv[i], fk);
+        Vec<T>::unpack(qv[i], fq[i]);
+        Vec<T>::unpack(kv[i], fk[i]);
+    }
+    if (a.layout == RPKV_ROPE_INTERLEAVED) {
 #pragma unroll
-        for (int e = 0; e < CH / 2; ++e) {
-            const float2 w = cs[i][e];
-            const float xq = fq[2 * e], yq = fq[2 * e + 1];
-            fq[2 * e] = xq * w.x - yq * w.y;
-            fq[2 * e + 1] = xq * w.y + yq * w.x;
-            const float xk = fk[2 * e], yk = fk[2 * e + 1];
-            fk[2 * e] = xk * w.x - yk * w.y;
-            fk[2 * e + 1] = xk * w.y + yk * w.x;
-        }
+        for (int i = 0; i < PER; ++i)
+#pragma unroll
+            for (int e = 0; e < CH / 2; ++e) {
+                const float2 w = cs[i * (CH / 2) + e];
+                const float xq = fq[i][2 * e], yq = fq[i][2 * e + 1];
+                fq[i][2 * e] = xq * w.x - yq * w.y;
+                fq[i][2 * e + 1] = xq * w.y + yq * w.x;
+                const float xk = fk[i][2 * e], yk = fk[i][2 * e + 1];
+                fk[i][2 * e] = xk * w.x - yk * w.y;
+                fk[i][2 * e + 1] = xk * w.y + yk * w.x;
+            }
+    } else {
+#pragma unroll
+        for (int j = 0; j < PER / 2; ++j)
+#pragma unroll
+            for (int e = 0; e < CH; ++e) {
+                const float2 w = cs[j * CH + e];
+                const float xq = fq[2 * j][e], yq = fq[2 * j + 1][e];
+                fq[2 * j][e] = xq * w.x - yq * w.y;
+                fq[2 * j + 1][e] = yq * w.x + xq * w.y;
+                const float xk = fk[2 * j][e], yk = fk[2 * j + 1][e];
+                fk[2 * j][e] = xk * w.x - yk * w.y;
+                fk[2 * j + 1][e] = yk * w.x + xk * w.y;
+            }
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        int r, c;
+        chunk_of<CH>(a, tid, i, r, c);
+        const bool valid = r < nrows;
         if (valid) {
-            *(uint4*)(qrb + r * rs + c * CH) = Vec<T>::pack(fq);
-            if (ok) *(uint4*)(kdst + r * kHeadDim + c * CH) = Vec<T>::pack(fk);
+            *(uint4*)(qrb + r * rs + c * CH) = Vec<T>::pack(fq[i]);
+            if (ok) *(uint4*)(kdst + r * kHeadDim + c * CH) = Vec<T>::pack(fk[i]);
         }
         // Rows past the tile's tokens are zeros (padding slots stay zero).
         const uint4 v = valid ? vv[i] : make_uint4(0, 0, 0, 0);

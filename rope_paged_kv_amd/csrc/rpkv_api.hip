@@ -25,16 +25,17 @@ namespace {
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool spec_ok(const rope3d_spec* r) {
-    return r && r->head_dim > 0 && r->head_dim % 2 == 0 && r->pairs_t >= 0 && r->pairs_h >= 0 &&
-           r->pairs_w >= 0 && r->pairs_t + r->pairs_h + r->pairs_w == r->head_dim / 2 &&
-           r->theta > 0 && r->ntk_factor > 0 && r->max_frames >= 1 && r->max_h >= 1 && r->max_w >= 1;
+    if (!r || r->head_dim <= 0 || r->head_dim % 2 || r->pairs_t < 0 || r->pairs_h < 0 || r->pairs_w < 0 ||
+        r->pairs_t + r->pairs_h + r->pairs_w != r->head_dim / 2 || !(r->theta > 0) ||
+        !(r->ntk_factor > 0) || r->max_frames < 1 || r->max_h < 1 || r->max_w < 1)
+        return false;
+    if (r->layout == RPKV_ROPE_HALF_SPLIT)
+        return r->pairs_t % 8 == 0 && r->pairs_h % 8 == 0 && r->pairs_w % 8 == 0;
+    return r->layout == RPKV_ROPE_INTERLEAVED;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
-// Picks the number of key-range splits of the bf16 attention: enough
-// workgroups to fill the chip about once (256 CUs x 4 resident workgroups),
-// without splits shorter than 8 key tiles at full cache occupancy.
 // Key-range splits of attend_frame.  The bf16 kernel is bound by what each
 // compute unit (256 on MI355X) issues, so a launch lasts about as long as
 // the most loaded unit needs for its ceil(workgroups / 256) workgroups, and
@@ -252,6 +253,7 @@ int kv_append_frame(kv_handle* h, int layer, int frame_idx, int commit, const vo
     a.pt = r.pairs_t;
     a.ph = r.pairs_h;
     a.pw = r.pairs_w;
+    a.layout = r.layout;
     a.frame = frame_idx;
     a.commit = commit;
     a.n_tiles = 1 + L.tpp;

@@ -75,6 +75,7 @@ struct AppendArgs {
     size_t kpool_elems, ksp_elems;
     int S, N, H, P, gw, nsp, pool, slot_cap, sp_cap, sp_page, sf, max_kf;
     int pt, ph, pw;
+    int layout;             // RPKV_ROPE_INTERLEAVED or RPKV_ROPE_HALF_SPLIT
     int frame, commit;
     int n_tiles;            // workgroups per (stream, head)
 };

@@ -50,6 +50,7 @@ class Workload:
     pairs: tuple = (12, 10, 10)             # complex pairs on the t, h, w axes
     theta: float = 10000.0
     ntk_factor: float = 1.0
+    rope_layout: int = 0                    # 0 interleaved pairs, 1 half-split axis blocks
     max_frames: Optional[int] = None        # rotary t-table length (default: frames)
     # Full-depth chain (frame layers interleaved with cached layers).
     chain_layers: int = 0   # 0: single cached layer fed by seeded q/k/v
@@ -124,6 +125,19 @@ def small_variants() -> dict:
         "small_chain": Workload("small_chain_6x6", "bf16", frames=7, grid_h=6, grid_w=6, heads=4,
                                 streams=2, cached_layers=2, scale_frames=1, sliding_window=2,
                                 keyframe_interval=2, chain_layers=4, hidden=256),
+        # the 2D module's arrangement: y and x halves, base frequency 100
+        "small_rope2d": Workload("small_rope2d_10x7", "bf16", frames=8, grid_h=10, grid_w=7, heads=2,
+                                 scale_frames=1, sliding_window=3, keyframe_interval=1,
+                                 pairs=(0, 16, 16), theta=100.0, rope_layout=1),
+        "small_rope2d_f32": Workload("small_rope2d_f32_5x6", "f32", frames=6, grid_h=5, grid_w=6,
+                                     heads=2, scale_frames=1, sliding_window=2, keyframe_interval=2,
+                                     pairs=(16, 8, 8), theta=100.0, rope_layout=1),
+        # NTK-stretched base
+        "small_ntk": Workload("small_ntk_8x8", "bf16", frames=6, grid_h=8, grid_w=8, heads=2,
+                              scale_frames=1, sliding_window=2, keyframe_interval=1, ntk_factor=4.0),
+        # a camera-head style grid: one patch per frame
+        "small_cam": Workload("small_cam_1x1", "bf16", frames=12, grid_h=1, grid_w=1, heads=2,
+                              scale_frames=2, sliding_window=3, keyframe_interval=1),
     }
 
 

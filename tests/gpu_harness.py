@@ -15,7 +15,7 @@ def torch_dtype(wl: Workload):
 def make_cache(wl: Workload, layers: int = 1, splits: int = 0, **over) -> rp.PagedKVCache:
     spec = rp.make_spec(pairs=wl.pairs, theta=wl.theta, ntk_factor=wl.ntk_factor,
                         max_frames=over.pop("max_frames", wl.t_rows),
-                        max_h=wl.grid_h, max_w=wl.grid_w)
+                        max_h=wl.grid_h, max_w=wl.grid_w, layout=wl.rope_layout)
     kw = dict(num_layers=layers, num_streams=wl.streams, num_heads=wl.heads, grid_h=wl.grid_h,
               grid_w=wl.grid_w, dtype=wl.dtype, head_dim=wl.head_dim,
               special_tokens=wl.n_special, patch_page_size=wl.page_size,

@@ -161,7 +161,8 @@ def _pages_for(cache, layer, s):
     return kp[layer, s], vp[layer, s], ks[layer, s], vs[layer, s]
 
 
-@pytest.mark.parametrize("name", ["small_bf16", "small_f32", "small_partial_sp", "tiny"])
+@pytest.mark.parametrize("name", ["small_bf16", "small_f32", "small_partial_sp", "tiny", "small_rope2d",
+                                  "small_rope2d_f32", "small_ntk", "small_cam"])
 def test_rope_append_matches_oracle(name):
     wl = WORKLOADS[0] if name == "tiny" else small_variants()[name]
     cache = make_cache(wl)

@@ -120,3 +120,96 @@ def test_round_bf16_matches_float32_bit_rounding():
     # exact ties go to even
     assert rope3d.round_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
     assert rope3d.round_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+
+
+# ---------------------------------------------------------------- half-split layout
+
+PAIRS_2D = (0, 16, 16)
+
+
+def rot_half(x, t, h, w, pairs=PAIRS_2D, theta=100.0):
+    tab = rope3d.rotation_table((np.array([t]), np.array([h]), np.array([w])), pairs, theta, 1.0)
+    return rope3d.apply_half_split(x.reshape(1, 1, -1), tab, pairs).reshape(-1)
+
+
+def rotate_half_rope(x: np.ndarray, pos: int, theta: float) -> np.ndarray:
+    """A 1D rotary embedding of a d-vector in the split-halves arrangement,
+    written as the matrix [[C, -S], [S, C]] with C, S = diag(cos, sin) of
+    pos * theta^(-2i/d), i < d/2 -- the rotate-half form of the 2D module."""
+    d = x.shape[-1]
+    a = pos * theta ** (-2.0 * np.arange(d // 2) / d)
+    c, s = np.diag(np.cos(a)), np.diag(np.sin(a))
+    r = np.block([[c, -s], [s, c]])
+    return r @ x
+
+
+def test_half_split_unit_vector_closed_form():
+    """e_i of the h block turns into cos(h*w_i) e_i + sin(h*w_i) e_{i+16},
+    w_i = 100^(-i/16): for i = 0 the angle is h, for i = 8 it is h/10."""
+    for i, omega in ((0, 1.0), (8, 0.1), (15, 100.0 ** (-15 / 16))):
+        x = np.zeros(64)
+        x[i] = 1.0
+        y = rot_half(x, 5, 3, 2)
+        want = np.zeros(64)
+        want[i] = math.cos(3 * omega)
+        want[i + 16] = math.sin(3 * omega)
+        assert np.allclose(y, want, atol=1e-14), i
+        # the w block (channels 32..63) takes the w coordinate
+        x = np.zeros(64)
+        x[32 + i] = 1.0
+        y = rot_half(x, 5, 3, 2)
+        want = np.zeros(64)
+        want[32 + i] = math.cos(2 * omega)
+        want[48 + i] = math.sin(2 * omega)
+        assert np.allclose(y, want, atol=1e-14), i
+
+
+@pytest.mark.parametrize("lo,axis", [(0, 1), (32, 2)])
+def test_half_split_block_is_rotate_half_rope(lo, axis):
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(64)
+    for p in (1, 4, 9, 63):
+        pos = [7, 0, 0]
+        pos[axis] = p
+        y = rot_half(x, *pos)
+        assert np.allclose(y[lo:lo + 32], rotate_half_rope(x[lo:lo + 32], p, 100.0), atol=1e-12)
+        other = slice(32, 64) if lo == 0 else slice(0, 32)
+        # the other block sees its own coordinate only (0 here)
+        assert np.allclose(y[other], x[other], atol=1e-12)
+
+
+def test_half_split_is_interleaved_after_a_channel_permutation():
+    """Moving channel (block + i, block + i + pairs_a) to the adjacent pair
+    (2(col + i), 2(col + i) + 1) turns the half-split rotation into the
+    interleaved one, for any split with a t block."""
+    pairs = (16, 8, 8)
+    perm = []
+    ch = 0
+    for n in pairs:
+        for i in range(n):
+            perm += [ch + i, ch + n + i]
+        ch += 2 * n
+    perm = np.array(perm)          # interleaved slot k holds half-split channel perm[k]
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal(64)
+    tab = rope3d.rotation_table((np.array([11]), np.array([4]), np.array([9])), pairs, 100.0, 1.0)
+    y_half = rope3d.apply_half_split(x.reshape(1, 1, -1), tab, pairs).reshape(-1)
+    y_int = rope3d.apply_rotary(x[perm].reshape(1, 1, -1), tab).reshape(-1)
+    assert np.allclose(y_half[perm], y_int, atol=1e-12)
+
+
+def test_half_split_relative_position_and_norm():
+    rng = np.random.default_rng(7)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    base = np.dot(rot_half(q, 0, 3, 5), rot_half(k, 0, 1, 2))
+    for d in ((0, 4, 1), (0, 10, 20), (0, 60, 33)):
+        moved = np.dot(rot_half(q, 0, 3 + d[1], 5 + d[2]), rot_half(k, 0, 1 + d[1], 2 + d[2]))
+        assert abs(moved - base) < 1e-10
+    y = rot_half(q, 0, 17, 29)
+    # norm of every rotating pair (i, i + 16) within each block
+    for lo in (0, 32):
+        for i in range(16):
+            a = np.hypot(q[lo + i], q[lo + i + 16])
+            b = np.hypot(y[lo + i], y[lo + i + 16])
+            assert abs(a - b) < 1e-12
+    assert np.allclose(rot_half(q, 0, 0, 0), q, atol=0)
