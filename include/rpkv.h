@@ -206,6 +206,25 @@ int kv_append_frame(kv_handle* h, int layer, int frame_idx, int commit, const vo
                     void* stream);
 
 /*
+ * kv_append_frame for a frame of its own patch grid (grid_h x grid_w, at
+ * most the configured grid_h*grid_w patches, grid_h <= rope.max_h and
+ * grid_w <= rope.max_w): the cache takes variable patch counts per frame
+ * ([ROPE-KV] FAQ on variable numbers of patches per frame: pages hold the
+ * valid tokens they were given, attention reads those only).
+ *   q, k, v, q_rot keep the [S][N][H][D] shape of the configuration; only
+ *   the frame's first special_tokens + grid_h*grid_w tokens are read, and
+ *   only those rows of q_rot are written.  Patch token p sits at
+ *   (frame_idx, p / grid_w, p % grid_w).
+ * The page records its token count; attend_frame then attends over the valid
+ * tokens of every visible page and answers this frame's tokens only (rows
+ * past them in out / lse are left as they were).  kv_append_frame is this
+ * call with the configured grid.  EINVAL on a grid outside those bounds.
+ */
+int kv_append_frame_grid(kv_handle* h, int layer, int frame_idx, int commit, int grid_h,
+                         int grid_w, const void* q, const void* k, const void* v, void* q_rot,
+                         const void* d_tables, void* stream);
+
+/*
  * Attention of the frame's N query tokens (all heads, all streams) over the
  * visible page table of `layer` ([ROPE-KV] "Attention Computation with Cached
  * RoPE"; [RT3D] "Per-Frame Processing and Causal Attention"):
@@ -252,6 +271,8 @@ typedef struct {
     int scale_pages[RPKV_MAX_POOL_PAGES];
     int window_pages[RPKV_MAX_POOL_PAGES]; /* oldest first */
     int visible_pages[RPKV_MAX_POOL_PAGES];
+    int query_tokens;           /* tokens of the last appended frame */
+    int page_tokens[RPKV_MAX_POOL_PAGES];  /* tokens stored in each pool page (0: never written) */
 } kv_state_host;
 
 /* Copies the state of cache (layer, stream_idx) after the work queued on

@@ -32,8 +32,12 @@ class OracleStream:
         return rope3d.round_bf16(x) if self.round else x
 
     def rotate(self, x: np.ndarray, frame: int) -> np.ndarray:
+        """Rotated tokens of the frame: its specials and its own patch grid
+        (rows of x past them are not part of the frame)."""
         wl = self.wl
-        return rope3d.rotate_frame(x, frame, wl.grid_h, wl.grid_w, wl.n_special, wl.pairs,
+        gh, gw = wl.grid_of(frame)
+        x = np.asarray(x)[:wl.n_special + gh * gw]
+        return rope3d.rotate_frame(x, frame, gh, gw, wl.n_special, wl.pairs,
                                    wl.theta, wl.ntk_factor, layout=wl.rope_layout)
 
     def q_rot(self, frame: int) -> np.ndarray:
@@ -44,7 +48,7 @@ class OracleStream:
         """(K rotated, V) of the frame as the cache holds them [N, H, D] (float64)."""
         if frame not in self._kv:
             k = self._store(self.rotate(self.source(frame, 1), frame))
-            v = np.asarray(self.source(frame, 2), dtype=np.float64)
+            v = np.asarray(self.source(frame, 2), dtype=np.float64)[:k.shape[0]]
             self._kv[frame] = (k, v)
         return self._kv[frame]
 

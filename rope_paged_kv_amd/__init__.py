@@ -72,6 +72,13 @@ def kv_append_frame(h, layer: int, frame_idx: int, commit: int, q, k, v, q_rot, 
                                 _vp(q_rot), _vp(d_tables), stream), "kv_append_frame")
 
 
+def kv_append_frame_grid(h, layer: int, frame_idx: int, commit: int, grid_h: int, grid_w: int,
+                         q, k, v, q_rot, d_tables, stream: int) -> None:
+    _check(_lib.kv_append_frame_grid(h, layer, frame_idx, int(commit), grid_h, grid_w, _vp(q),
+                                     _vp(k), _vp(v), _vp(q_rot), _vp(d_tables), stream),
+           "kv_append_frame_grid")
+
+
 def attend_frame(h, layer: int, q_rot, out, lse, stream: int) -> None:
     _check(_lib.attend_frame(h, layer, _vp(q_rot), _vp(out), _vp(lse), stream), "attend_frame")
 
@@ -92,6 +99,8 @@ def kv_read_state(h, layer: int, stream_idx: int, stream: int) -> dict:
     out["scale_pages"] = list(st.scale_pages[:st.n_scale])
     out["window_pages"] = list(st.window_pages[:st.n_window])
     out["visible_pages"] = list(st.visible_pages[:st.n_visible_pages])
+    out["query_tokens"] = st.query_tokens
+    out["page_tokens"] = list(st.page_tokens)
     return out
 
 
@@ -165,8 +174,14 @@ class PagedKVCache:
     def reset(self, layer: int = -1):
         kv_reset(self.h, layer, self.stream)
 
-    def append(self, layer, frame_idx, commit, q, k, v, q_rot):
-        kv_append_frame(self.h, layer, frame_idx, commit, q, k, v, q_rot, self.tables, self.stream)
+    def append(self, layer, frame_idx, commit, q, k, v, q_rot, grid=None):
+        """grid: this frame's (grid_h, grid_w) if it differs from the configured one."""
+        if grid is None:
+            kv_append_frame(self.h, layer, frame_idx, commit, q, k, v, q_rot, self.tables,
+                            self.stream)
+        else:
+            kv_append_frame_grid(self.h, layer, frame_idx, commit, grid[0], grid[1], q, k, v,
+                                 q_rot, self.tables, self.stream)
 
     def attend(self, layer, q_rot, out, lse=None):
         attend_frame(self.h, layer, q_rot, out, lse, self.stream)

@@ -19,8 +19,8 @@ namespace rpkv {
 
 template <typename T>
 __device__ inline void tile_ref(const AttnArgs& a, int s, int h, int t, int n_patch_tiles,
-                                const int* vis, int vis_sp, const T*& k, const T*& v,
-                                int& vstride, int& len) {
+                                const int* vis, const int* vis_len, int vis_sp, const T*& k,
+                                const T*& v, int& vstride, int& len) {
     if (t < n_patch_tiles) {
         const int pi = t / a.tpp;
         const int off = (t - pi * a.tpp) * kTile;
@@ -29,7 +29,7 @@ __device__ inline void tile_ref(const AttnArgs& a, int s, int h, int t, int n_pa
         k = (const T*)a.kpool + s * a.kpool_elems + (pg * a.slot_cap + off) * kHeadDim;
         v = (const T*)a.vpool + s * a.kpool_elems + pg * kHeadDim * a.slot_cap + off;
         vstride = a.slot_cap;
-        len = min(kTile, a.P - off);
+        len = min(kTile, vis_len[pi] - off);   // a page holds the tokens its frame had
     } else {
         const int off = (t - n_patch_tiles) * kTile;
         k = (const T*)a.ksp + s * a.ksp_elems + ((size_t)h * a.sp_cap + off) * kHeadDim;
@@ -52,6 +52,7 @@ __global__ __launch_bounds__(256) void k_attend_combine(AttnArgs a) {
     const int q = rest % a.N;
     const int sh = rest / a.N;   // s*H + h
     const int s = sh / a.H, h = sh % a.H;
+    if (q >= a.states[s].n_query) return;   // not a token of this frame
     const size_t base = (size_t)sh * a.splits * a.N + q;
     float mx = -INFINITY;
     for (int i = 0; i < a.splits; ++i) mx = fmaxf(mx, a.part_lse[base + (size_t)i * a.N]);
@@ -91,9 +92,9 @@ __global__ __launch_bounds__(64) void k_attend_f32(AttnArgs a) {
     __shared__ float ks[kTile][kHeadDim + 1];
     __shared__ float vs[kHeadDim][kTile + 1];
     const int h = blockIdx.y, s = blockIdx.z, tid = threadIdx.x;
-    const int q = blockIdx.x * 64 + tid;
-    const bool qvalid = q < a.N;
     const CacheState* st = a.states + s;
+    const int q = blockIdx.x * 64 + tid;
+    const bool qvalid = q < st->n_query;
     const int vis_n = st->vis_n, vis_sp = st->vis_sp_tokens;
     const int n_patch_tiles = vis_n * a.tpp;
     const int n_tiles = n_patch_tiles + (vis_sp + kTile - 1) / kTile;
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(64) void k_attend_f32(AttnArgs a) {
         const float* kp;
         const float* vp;
         int vstride, len;
-        tile_ref<float>(a, s, h, t, n_patch_tiles, st->vis, vis_sp, kp, vp, vstride, len);
+        tile_ref<float>(a, s, h, t, n_patch_tiles, st->vis, st->vis_len, vis_sp, kp, vp, vstride, len);
         __syncthreads();
         // 16-byte loads, all issued before the LDS stores: thread tid takes
         // float4 chunks tid, tid+64, ... of the K tile and of the V^T tile.

@@ -233,6 +233,7 @@ __device__ __forceinline__ void step(f32x16& sc, f32x16& nxt, const char* vt, in
 
 __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+    __shared__ int s_vlen[kMaxPool];   // tokens of each visible patch page
     char* const kring = lds;
     char* const vring = lds + kKStages * kTileBytes;
 
@@ -252,6 +253,10 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     const int hh = lane >> 5, col = lane & 31;
     const CacheState* st = a.states + s;
+    // The frame's own tokens are the queries: a q-tile wholly past them has
+    // nothing to do.
+    const int n_q = uniform(st->n_query);
+    if (qt * kQB >= n_q) return;
     const int vis_n = uniform(st->vis_n);
     const int vis_sp = uniform(st->vis_sp_tokens);
 
@@ -303,7 +308,7 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
     // Q^T operands of this wave's 32 queries (B operand: column = query): the
     // stored bf16 values as they are.
     const int q = qt * kQB + wave * kQW + col;
-    const bool qvalid = q < a.N;
+    const bool qvalid = q < n_q;
     bf16x8 qf[4];
     {
         const uint16_t* qp = (const uint16_t*)a.q + (((size_t)s * a.N + (qvalid ? q : 0)) * a.H + h) * kHeadDim;
@@ -332,7 +337,14 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) foff[j] = col * 128 + (((2 * j + hh) ^ ((col >> 1) & 7)) << 4);
 
-    // Prologue: tiles 0 and 1 in flight; wait for tile 0.
+    // Page lengths: all P when every visible page holds a whole grid (then
+    // nothing is read per tile), else an LDS copy.
+    const bool vis_full = uniform(st->vis_full) != 0;
+    if (!vis_full)
+        for (int i = tid; i < vis_n; i += 256) s_vlen[i] = st->vis_len[i];
+
+    // Prologue: tiles 0 and 1 in flight; wait for tile 0 (the barrier also
+    // publishes s_vlen).
     if (n > 0) ld.issue(t0, kring, vring, wave);
     if (n > 1) ld.issue(t0 + 1, kring + kTileBytes, vring + kTileBytes, wave);
     if (n > 1)
@@ -344,6 +356,15 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
     // sA: first half of the tile being computed, sB: its second half.  The
     // products of a half are formed one half ahead of its softmax; past the
     // last tile they read a stale stage and are never used.
+    // Valid keys of tile t: a patch page holds the tokens its frame had
+    // (tiles past them have none), the special stream vis_sp.  Read one tile
+    // ahead from an LDS copy of the page lengths.
+    auto tile_len = [&](int t) {
+        if (t >= n_patch_tiles) return min(kTile, vis_sp - (t - n_patch_tiles) * kTile);
+        const int plen = vis_full ? a.P : s_vlen[t / a.tpp];
+        return min(kTile, plen - (t % a.tpp) * kTile);
+    };
+    int len_next = uniform(tile_len(t0));
     f32x16 sA = scores(kring, 0, foff, qf);
     f32x16 sB;
     // Tiles in groups of kGroup, so every stage offset is a constant that
@@ -356,9 +377,9 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
             const char* kcur = kring + (u % kKStages) * kTileBytes;
             const char* knxt = kring + ((u + 1) % kKStages) * kTileBytes;
             const char* vcur = vring + (u % kVStages) * kTileBytes;
-            const int len = uniform(t < n_patch_tiles ? min(kTile, a.P - (t % a.tpp) * kTile)
-                                                      : min(kTile, vis_sp - (t - n_patch_tiles) * kTile));
-            step(sA, sB, vcur, 0, len, kcur + kHalfBytes, foff, qf, hh, A);
+            const int len = len_next;
+            len_next = uniform(tile_len(t + 1));
+            if (len > 0) step(sA, sB, vcur, 0, len, kcur + kHalfBytes, foff, qf, hh, A);
             if (i + 1 < n) {
                 // Tile i+1 landed for every wave, every wave is done with K of
                 // tile i and V^T of tile i-1: their stages take tile i+2.

@@ -24,8 +24,11 @@ __global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t nt
 
 __global__ void k_reset(CacheState* states, int count) {
     int c = blockIdx.x;
-    if (c >= count || threadIdx.x != 0) return;
+    if (c >= count) return;
     CacheState* s = states + c;
+    for (int i = threadIdx.x; i < kMaxPool; i += blockDim.x) s->page_tokens[i] = 0;
+    if (threadIdx.x != 0) return;
+    s->n_query = 0;
     s->pending = 0;
     s->status = RPKV_OK;
     s->fresh = 0;

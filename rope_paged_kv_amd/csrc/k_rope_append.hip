@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
 
     const bool special = tile == 0;
     const int slot0 = special ? 0 : (tile - 1) * kTile;
-    const int nrows = special ? a.nsp : min(kTile, a.P - slot0);
+    const int nrows = special ? a.nsp : min(kTile, a.fP - slot0);   // may be <= 0: a tile past the frame's patches
     const int tok0 = special ? 0 : a.nsp + slot0;
 
     const size_t rs = (size_t)a.H * kHeadDim;  // elements between consecutive tokens
@@ -172,9 +172,9 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
         chunk_of<CH>(a, tid, i, r, c);
         int hp = 0, wp = 0;   // specials sit at h = w = 0
         if (!special) {
-            const int p = slot0 + (r < nrows ? r : 0);
-            hp = p / a.gw;
-            wp = p - hp * a.gw;
+            const int p = r < nrows ? slot0 + r : 0;   // rows past the frame's patches: (0, 0)
+            hp = p / a.fgw;
+            wp = p - hp * a.fgw;
         }
         if (a.layout == RPKV_ROPE_INTERLEAVED) {
 #pragma unroll
@@ -284,9 +284,18 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
     // own page (it comes last whether it will be committed or not).
     const int ns = st->n_scale, nw = st->n_win, head = st->win_head;
     const int vis_n = ok ? ns + nw + 1 : 0;
-    for (int i = tid; i < vis_n; i += 256)
-        st->vis[i] = i < ns ? st->scale[i] : (i < ns + nw ? st->win[(head + i - ns) % kMaxPool] : page);
+    int full = 1;
+    for (int i = tid; i < vis_n; i += 256) {
+        const int pg = i < ns ? st->scale[i] : (i < ns + nw ? st->win[(head + i - ns) % kMaxPool] : page);
+        st->vis[i] = pg;
+        const int len = i < ns + nw ? st->page_tokens[pg] : a.fP;
+        st->vis_len[i] = len;
+        full &= len == a.P;
+    }
+    full = __syncthreads_and(full);
     if (tid == 0) {
+        st->n_query = a.nsp + a.fP;
+        st->vis_full = full;
         if (!ok) {
             if (status == RPKV_OK) st->status = RPKV_ENOSPACE;
             st->vis_n = 0;
@@ -299,6 +308,7 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
             const int sp_pages = (vis_sp + a.sp_page - 1) / a.sp_page;
             st->target = page;
             st->sp_off = sp_off;
+            st->page_tokens[page] = a.fP;
             st->vis_n = vis_n;
             st->vis_sp_tokens = vis_sp;
             st->vis_sp_pages = sp_pages;

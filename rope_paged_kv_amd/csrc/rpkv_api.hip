@@ -214,8 +214,19 @@ int kv_reset(kv_handle* h, int layer, void* stream) {
 int kv_append_frame(kv_handle* h, int layer, int frame_idx, int commit, const void* q,
                     const void* k, const void* v, void* q_rot, const void* d_tables,
                     void* stream) {
+    if (!h) return RPKV_EINVAL;
+    return kv_append_frame_grid(h, layer, frame_idx, commit, h->cfg.grid_h, h->cfg.grid_w, q, k, v,
+                                q_rot, d_tables, stream);
+}
+
+int kv_append_frame_grid(kv_handle* h, int layer, int frame_idx, int commit, int grid_h,
+                         int grid_w, const void* q, const void* k, const void* v, void* q_rot,
+                         const void* d_tables, void* stream) {
     if (!h || layer < 0 || layer >= h->cfg.num_layers) return RPKV_EINVAL;
     if (frame_idx < 0 || frame_idx >= h->cfg.rope.max_frames || (commit != 0 && commit != 1))
+        return RPKV_EINVAL;
+    if (grid_h < 1 || grid_w < 1 || grid_h > h->cfg.rope.max_h || grid_w > h->cfg.rope.max_w ||
+        (long long)grid_h * grid_w > h->L.P)
         return RPKV_EINVAL;
     if (!q || !k || !v || !q_rot || !d_tables) return RPKV_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_rot) || !aligned16(d_tables))
@@ -243,6 +254,8 @@ int kv_append_frame(kv_handle* h, int layer, int frame_idx, int commit, const vo
     a.H = L.H;
     a.P = L.P;
     a.gw = L.gw;
+    a.fP = grid_h * grid_w;
+    a.fgw = grid_w;
     a.nsp = L.nsp;
     a.pool = L.pool;
     a.slot_cap = L.slot_cap;
@@ -345,6 +358,8 @@ int kv_read_state(kv_handle* h, int layer, int stream_idx, kv_state_host* out, v
     for (int i = 0; i < tmp->n_win && i < kMaxPool; ++i)
         out->window_pages[i] = tmp->win[(tmp->win_head + i) % kMaxPool];
     for (int i = 0; i < tmp->vis_n && i < kMaxPool; ++i) out->visible_pages[i] = tmp->vis[i];
+    out->query_tokens = tmp->n_query;
+    for (int i = 0; i < h->L.pool && i < kMaxPool; ++i) out->page_tokens[i] = tmp->page_tokens[i];
     free(tmp);
     return RPKV_OK;
 }

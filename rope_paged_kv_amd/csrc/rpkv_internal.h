@@ -31,11 +31,14 @@ struct CacheState {
     int vis_sp_pages;   // special pages 0 .. vis_sp_pages-1 visible
     int last_page_len;  // valid tokens in the last visible special page
     int vis_sp_tokens;  // visible special tokens
-    int pad[2];
+    int n_query;        // tokens of the last appended frame (specials + its patches)
+    int vis_full;       // 1: every visible patch page holds a whole grid (P tokens)
     int free_[kMaxPool];
     int scale[kMaxPool];
     int win[kMaxPool];  // ring buffer of capacity kMaxPool
     int vis[kMaxPool];  // visible patch pages in attention order
+    int vis_len[kMaxPool];      // tokens of each visible patch page
+    int page_tokens[kMaxPool];  // tokens stored in each pool page (its frame's patches)
 };
 
 // Storage position <-> key index inside an aligned group of 16 slots of a
@@ -74,6 +77,7 @@ struct AppendArgs {
     char* vsp;
     size_t kpool_elems, ksp_elems;
     int S, N, H, P, gw, nsp, pool, slot_cap, sp_cap, sp_page, sf, max_kf;
+    int fP, fgw;            // this frame's patches (<= P) and its grid width
     int pt, ph, pw;
     int layout;             // RPKV_ROPE_INTERLEAVED or RPKV_ROPE_HALF_SPLIT
     int frame, commit;

@@ -51,6 +51,7 @@ class Workload:
     theta: float = 10000.0
     ntk_factor: float = 1.0
     rope_layout: int = 0                    # 0 interleaved pairs, 1 half-split axis blocks
+    grids: tuple = ()                       # per-frame (gh, gw), cycled; () = the grid above
     max_frames: Optional[int] = None        # rotary t-table length (default: frames)
     # Full-depth chain (frame layers interleaved with cached layers).
     chain_layers: int = 0   # 0: single cached layer fed by seeded q/k/v
@@ -76,6 +77,14 @@ class Workload:
     @property
     def key(self) -> int:
         return zlib.crc32(self.name.encode()) & 0x7FFFFFFF
+
+    def grid_of(self, f: int) -> tuple:
+        """Patch grid of frame f (a frame may have fewer patches than the page holds)."""
+        return self.grids[f % len(self.grids)] if self.grids else (self.grid_h, self.grid_w)
+
+    def frame_tokens(self, f: int) -> int:
+        gh, gw = self.grid_of(f)
+        return self.n_special + gh * gw
 
     def is_keyframe(self, f: int) -> bool:
         return f % self.keyframe_interval == 0
@@ -135,6 +144,10 @@ def small_variants() -> dict:
         # NTK-stretched base
         "small_ntk": Workload("small_ntk_8x8", "bf16", frames=6, grid_h=8, grid_w=8, heads=2,
                               scale_frames=1, sliding_window=2, keyframe_interval=1, ntk_factor=4.0),
+        # frames of their own patch grids, up to 9x11 (partial patch pages)
+        "small_vargrid": Workload("small_vargrid_9x11", "bf16", frames=10, grid_h=9, grid_w=11,
+                                  heads=3, scale_frames=2, sliding_window=3, keyframe_interval=1,
+                                  grids=((9, 11), (7, 11), (5, 6), (1, 1), (9, 7))),
         # a camera-head style grid: one patch per frame
         "small_cam": Workload("small_cam_1x1", "bf16", frames=12, grid_h=1, grid_w=1, heads=2,
                               scale_frames=2, sliding_window=3, keyframe_interval=1),

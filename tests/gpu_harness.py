@@ -43,7 +43,8 @@ class Runner:
 
     def frame(self, f: int, q, k, v, commit: bool, evict: bool = True):
         c = self.cache
-        c.append(self.layer, f, int(commit), q, k, v, self.q_rot)
+        grid = self.wl.grid_of(f) if self.wl.grids else None
+        c.append(self.layer, f, int(commit), q, k, v, self.q_rot, grid=grid)
         c.attend(self.layer, self.q_rot, self.out, self.lse)
         if evict:
             c.evict(self.layer)

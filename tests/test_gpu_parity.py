@@ -222,7 +222,7 @@ def run_and_compare(wl, frames_to_check, rows=None, splits=0, heads=None, stream
         if f not in frames_to_check:
             continue
         torch.cuda.synchronize()
-        r = np.arange(wl.tokens) if rows is None else np.asarray(rows(f))
+        r = np.arange(wl.frame_tokens(f)) if rows is None else np.asarray(rows(f))
         hs = np.arange(wl.heads) if heads is None else np.asarray(heads)
         got = run.out.float().cpu().numpy()
         got_lse = run.lse.cpu().numpy()
@@ -270,6 +270,56 @@ def test_single_layer_37x37_sampled():
     frames = {0, 1, 7, 8, 23, 24, 25, 40, 63}
     worst, worst_lse = run_and_compare(wl, frames, rows=sampled_rows(wl))
     print(f"37x37 single layer: max|out-oracle| {worst:.3e}  max|lse-oracle| {worst_lse:.3e}")
+
+
+def test_variable_patch_grids():
+    """Frames of their own grids (9x11, 7x11, 5x6, 1x1, 9x7 in a 9x11 page):
+    pages record their token counts, q_rot and K follow each frame's grid,
+    attention reads the valid tokens of every page and answers the frame's
+    own tokens only (the rows past them keep what they held)."""
+    wl = small_variants()["small_vargrid"]
+    cache = make_cache(wl)
+    run = Runner(wl, cache)
+    sim = sim_for(wl)
+    orc = OracleStream(wl, lambda f, t: qkv(wl, 0, 0, f, t))
+    ns = wl.n_special
+    for f in range(wl.frames):
+        gh, gw = wl.grid_of(f)
+        n = ns + gh * gw
+        commit = wl.is_keyframe(f)
+        q, k, v = run.inputs(f)
+        run.out.fill_(7.0)
+        run.lse.fill_(7.0)
+        run.frame(f, q, k, v, commit, evict=False)
+        sim.append(f, commit)
+        st = cache.state(0, 0)
+        assert st["query_tokens"] == n, f
+        want_pt = {p: wl.grid_of(g)[0] * wl.grid_of(g)[1] for p, g in sim.page_frame.items()}
+        want_pt[sim.target] = gh * gw
+        for p, cnt in want_pt.items():
+            assert st["page_tokens"][p] == cnt, (f, p)
+        torch.cuda.synchronize()
+        got_q = run.q_rot[0, :n].float().cpu().numpy()
+        assert np.abs(got_q - orc.q_rot(f)).max() <= BF16_TOL, f
+        kp = _pages_for(cache, 0, 0)[0]
+        got_k = kp[:, sim.target, :gh * gw].float().cpu().numpy().transpose(1, 0, 2)
+        assert np.abs(got_k - orc.kv(f)[0][ns:]).max() <= BF16_TOL, f
+        o, lse = orc.attend(f)
+        assert np.abs(run.out[0, :n].float().cpu().numpy() - o).max() <= BF16_TOL, f
+        assert np.abs(run.lse[0, :, :n].cpu().numpy() - lse).max() <= LSE_TOL, f
+        assert torch.all(run.out[0, n:] == 7.0) and torch.all(run.lse[0, :, n:] == 7.0), f
+        sim.evict()
+        cache.evict(0)
+
+
+def test_append_grid_is_checked():
+    wl = small_variants()["small_vargrid"]
+    cache = make_cache(wl)
+    run = Runner(wl, cache)
+    q, k, v = run.inputs(0)
+    for grid in ((10, 11), (9, 12), (0, 5), (12, 9)):
+        with pytest.raises(rp.RpkvError):
+            cache.append(0, 0, 1, q, k, v, run.q_rot, grid=grid)
 
 
 def test_attention_large_logits_move_the_reference_max():
