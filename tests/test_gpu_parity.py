@@ -409,6 +409,54 @@ def test_visibility_probe_q_zero():
         cache.evict(0)
 
 
+def test_hip_graph_replays_follow_the_device_bookkeeping():
+    """attend_frame captured once in a HIP graph (main kernel and split
+    merge), then replayed after each eager append as the cache fills, evicts
+    and recycles: every replay equals an eager call on the same state.  A
+    whole frame step (append, attend, evict) captured and replayed equals the
+    eager step too.  Nothing on the path synchronises with the host."""
+    wl = small_variants()["small_skip"]
+    cache = make_cache(wl, splits=3)
+    run = Runner(wl, cache)
+    out_g = torch.empty_like(run.out)
+    lse_g = torch.empty_like(run.lse)
+    q, k, v = run.inputs(0)
+    cache.append(0, 0, 1, q, k, v, run.q_rot)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cache.attend(0, run.q_rot, out_g, lse_g)
+    cache.evict(0)
+    for f in range(1, wl.frames):
+        q, k, v = run.inputs(f)
+        cache.append(0, f, int(wl.is_keyframe(f)), q, k, v, run.q_rot)
+        g.replay()
+        cache.attend(0, run.q_rot, run.out, run.lse)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, run.out) and torch.equal(lse_g, run.lse), f
+        cache.evict(0)
+
+    # a whole step captured for frame F, replayed after eager frames 0..F-1
+    F = 7
+    eager = make_cache(wl, splits=3)
+    graphed = make_cache(wl, splits=3)
+    re, rg = Runner(wl, eager), Runner(wl, graphed)
+    for f in range(F):
+        q, k, v = re.inputs(f)
+        re.frame(f, q, k, v, wl.is_keyframe(f))
+        rg.frame(f, q, k, v, wl.is_keyframe(f))
+    q, k, v = re.inputs(F)
+    torch.cuda.synchronize()
+    gs = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gs):
+        rg.frame(F, q, k, v, wl.is_keyframe(F))
+    gs.replay()
+    re.frame(F, q, k, v, wl.is_keyframe(F))
+    torch.cuda.synchronize()
+    assert torch.equal(rg.out, re.out) and torch.equal(rg.lse, re.lse)
+    assert graphed.state(0, 0) == eager.state(0, 0)
+
+
 def test_replay_is_bitwise_deterministic():
     wl = small_variants()["small_skip"]
     outs = []
