@@ -163,7 +163,9 @@ __device__ __forceinline__ void step(f32x16& sc, f32x16& nxt, const char* vt, in
     const float md = max3f(sc[9], sc[10], sc[11]);
     const float me = max3f(sc[12], sc[13], sc[14]);
     const float mx = max3f(max3f(ma, mb, mc), fmaxf(md, me), sc[15]);
-    if (A.first || __any(fmaf(mx, A.c, -A.M) > 8.f)) {
+    // (A half with no valid key -- a tile past a short page's tokens -- has
+    // every score at -inf: it moves nothing and adds nothing.)
+    if ((A.first && __any(mx > -INFINITY)) || __any(fmaf(mx, A.c, -A.M) > 8.f)) {
         // rare: move M (jointly for both lanes of a query; never down after
         // the first half tile) and rescale what was accumulated.
         const float d = fmaxf(mx, __shfl_xor(mx, 32)) * A.c;
@@ -356,15 +358,25 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
     // sA: first half of the tile being computed, sB: its second half.  The
     // products of a half are formed one half ahead of its softmax; past the
     // last tile they read a stale stage and are never used.
-    // Valid keys of tile t: a patch page holds the tokens its frame had
-    // (tiles past them have none), the special stream vis_sp.  Read one tile
-    // ahead from an LDS copy of the page lengths.
-    auto tile_len = [&](int t) {
-        if (t >= n_patch_tiles) return min(kTile, vis_sp - (t - n_patch_tiles) * kTile);
-        const int plen = vis_full ? a.P : s_vlen[t / a.tpp];
-        return min(kTile, plen - (t % a.tpp) * kTile);
+    // Valid keys of a tile: a patch page holds the tokens its frame had
+    // (tiles past them have none), the special stream vis_sp.  Worked out
+    // one tile ahead from a walk over (page, tile in page); the page length
+    // is looked up once per page, and not at all when every page is whole.
+    auto page_len = [&](int pi) { return vis_full ? a.P : uniform(s_vlen[pi]); };
+    int wpi = t0 / a.tpp, wti = t0 % a.tpp;   // walk position: the next tile
+    int wpl = wpi < vis_n ? page_len(wpi) : 0;
+    auto walk_len = [&](int t) {
+        return t < n_patch_tiles ? min(kTile, wpl - wti * kTile)
+                                 : min(kTile, vis_sp - (t - n_patch_tiles) * kTile);
     };
-    int len_next = uniform(tile_len(t0));
+    auto walk_next = [&]() {
+        if (++wti == a.tpp) {
+            wti = 0;
+            ++wpi;
+            if (wpi < vis_n) wpl = page_len(wpi);
+        }
+    };
+    int len_next = walk_len(t0);
     f32x16 sA = scores(kring, 0, foff, qf);
     f32x16 sB;
     // Tiles in groups of kGroup, so every stage offset is a constant that
@@ -378,8 +390,9 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
             const char* knxt = kring + ((u + 1) % kKStages) * kTileBytes;
             const char* vcur = vring + (u % kVStages) * kTileBytes;
             const int len = len_next;
-            len_next = uniform(tile_len(t + 1));
-            if (len > 0) step(sA, sB, vcur, 0, len, kcur + kHalfBytes, foff, qf, hh, A);
+            walk_next();
+            len_next = walk_len(t + 1);
+            step(sA, sB, vcur, 0, len, kcur + kHalfBytes, foff, qf, hh, A);
             if (i + 1 < n) {
                 // Tile i+1 landed for every wave, every wave is done with K of
                 // tile i and V^T of tile i-1: their stages take tile i+2.

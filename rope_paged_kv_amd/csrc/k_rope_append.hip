@@ -87,10 +87,10 @@ __device__ inline float2 coeff(const AppendArgs& a, int j, int hp, int wp) {
 // 2j+1 are a pair of chunks that rotate together -- a chunk of the first half
 // of an axis block and the chunk pairs_a channels after it -- and the pair
 // slots walk the tile's first-half chunks in order (cpr/2 per row).
-template <int CH>
+template <int CH, int LAYOUT>
 __device__ inline void chunk_of(const AppendArgs& a, int tid, int i, int& r, int& c) {
     constexpr int CPR = kHeadDim / CH;
-    if (a.layout == RPKV_ROPE_INTERLEAVED) {
+    if (LAYOUT == RPKV_ROPE_INTERLEAVED) {
         const int id = tid + i * 256;
         r = id / CPR;
         c = id % CPR;
@@ -117,9 +117,9 @@ __device__ inline void chunk_of(const AppendArgs& a, int tid, int i, int& r, int
 
 // Rotation coefficients of a thread's chunk slots, flat: interleaved, pair e
 // of slot i at [i*CH/2 + e]; half-split, channel e of pair slot j at [j*CH + e].
-template <int CH>
+template <int CH, int LAYOUT>
 __device__ inline float2 coeff_of(const AppendArgs& a, int c, int e, int hp, int wp) {
-    if (a.layout == RPKV_ROPE_INTERLEAVED) return coeff(a, c * (CH / 2) + e, hp, wp);
+    if (LAYOUT == RPKV_ROPE_INTERLEAVED) return coeff(a, c * (CH / 2) + e, hp, wp);
     // half-split: chunk c of the first half of its axis block; pair index
     // inside the axis = channel offset from the block start.
     const int nt = a.pt / CH, nh = a.ph / CH;
@@ -128,7 +128,7 @@ __device__ inline float2 coeff_of(const AppendArgs& a, int c, int e, int hp, int
     return a.tab_w[wp * a.pw + (c - 2 * (nt + nh)) * CH + e];
 }
 
-template <typename T>
+template <typename T, int LAYOUT>
 __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
     constexpr int CH = Vec<T>::kCh;        // elements per 16-byte chunk
     constexpr int CPR = kHeadDim / CH;     // chunks per row
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         int r, c;
-        chunk_of<CH>(a, tid, i, r, c);
+        chunk_of<CH, LAYOUT>(a, tid, i, r, c);
         const size_t off = (size_t)(r < nrows ? r : 0) * rs + c * CH;
         qv[i] = *(const uint4*)(qb + off);
         kv[i] = *(const uint4*)(kb + off);
@@ -169,19 +169,19 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         int r, c;
-        chunk_of<CH>(a, tid, i, r, c);
+        chunk_of<CH, LAYOUT>(a, tid, i, r, c);
         int hp = 0, wp = 0;   // specials sit at h = w = 0
         if (!special) {
             const int p = r < nrows ? slot0 + r : 0;   // rows past the frame's patches: (0, 0)
             hp = p / a.fgw;
             wp = p - hp * a.fgw;
         }
-        if (a.layout == RPKV_ROPE_INTERLEAVED) {
+        if (LAYOUT == RPKV_ROPE_INTERLEAVED) {
 #pragma unroll
-            for (int e = 0; e < CH / 2; ++e) cs[i * (CH / 2) + e] = coeff_of<CH>(a, c, e, hp, wp);
+            for (int e = 0; e < CH / 2; ++e) cs[i * (CH / 2) + e] = coeff_of<CH, LAYOUT>(a, c, e, hp, wp);
         } else if ((i & 1) == 0) {
 #pragma unroll
-            for (int e = 0; e < CH; ++e) cs[(i >> 1) * CH + e] = coeff_of<CH>(a, c, e, hp, wp);
+            for (int e = 0; e < CH; ++e) cs[(i >> 1) * CH + e] = coeff_of<CH, LAYOUT>(a, c, e, hp, wp);
         }
     }
 
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
         Vec<T>::unpack(qv[i], fq[i]);
         Vec<T>::unpack(kv[i], fk[i]);
     }
-    if (a.layout == RPKV_ROPE_INTERLEAVED) {
+    if (LAYOUT == RPKV_ROPE_INTERLEAVED) {
 #pragma unroll
         for (int i = 0; i < PER; ++i)
 #pragma unroll
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         int r, c;
-        chunk_of<CH>(a, tid, i, r, c);
+        chunk_of<CH, LAYOUT>(a, tid, i, r, c);
         const bool valid = r < nrows;
         if (valid) {
             *(uint4*)(qrb + r * rs + c * CH) = Vec<T>::pack(fq[i]);
@@ -320,10 +320,18 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
 
 hipError_t launch_rope_append(const AppendArgs& a, int dtype, hipStream_t st) {
     dim3 grid(a.n_tiles, a.H, a.S);
-    if (dtype == RPKV_BF16)
-        hipLaunchKernelGGL(k_rope_append<uint16_t>, grid, dim3(256), 0, st, a);
-    else
-        hipLaunchKernelGGL(k_rope_append<float>, grid, dim3(256), 0, st, a);
+    const bool half = a.layout == RPKV_ROPE_HALF_SPLIT;
+    if (dtype == RPKV_BF16) {
+        if (half)
+            hipLaunchKernelGGL((k_rope_append<uint16_t, RPKV_ROPE_HALF_SPLIT>), grid, dim3(256), 0, st, a);
+        else
+            hipLaunchKernelGGL((k_rope_append<uint16_t, RPKV_ROPE_INTERLEAVED>), grid, dim3(256), 0, st, a);
+    } else {
+        if (half)
+            hipLaunchKernelGGL((k_rope_append<float, RPKV_ROPE_HALF_SPLIT>), grid, dim3(256), 0, st, a);
+        else
+            hipLaunchKernelGGL((k_rope_append<float, RPKV_ROPE_INTERLEAVED>), grid, dim3(256), 0, st, a);
+    }
     return hipGetLastError();
 }
 
