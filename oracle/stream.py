@@ -21,8 +21,14 @@ Source = Callable[[int, int], np.ndarray]   # (frame, tensor 0/1/2) -> [N, H, D]
 
 class OracleStream:
     def __init__(self, wl, source: Source, keyframe_interval: Optional[int] = None,
-                 storage_round: Optional[bool] = None):
+                 storage_round: Optional[bool] = None, window_start: int = 0):
+        """window_start: first frame of the cache's life.  Windowed inference
+        starts every window on a fresh cache (page "KV Caching Benefits in
+        Ling Bot-Map", section "Cross-Window Alignment for Long Videos"), so
+        only frames from there on can be retained; frames keep their global
+        index as the temporal position."""
         self.wl = wl
+        self.window_start = window_start
         self.source = source
         self.interval = wl.keyframe_interval if keyframe_interval is None else keyframe_interval
         self.round = (wl.dtype == "bf16") if storage_round is None else storage_round
@@ -53,7 +59,7 @@ class OracleStream:
         return self._kv[frame]
 
     def stored_before(self, frame: int):
-        return retained.keyframes_before(frame, self.interval)
+        return [k for k in retained.keyframes_before(frame, self.interval) if k >= self.window_start]
 
     def visible(self, frame: int):
         wl = self.wl

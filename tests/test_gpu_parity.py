@@ -409,6 +409,26 @@ def test_visibility_probe_q_zero():
         cache.evict(0)
 
 
+def test_windowed_inference_restarts_on_a_fresh_cache():
+    """Windows of 7 frames (not a multiple of the keyframe interval): kv_reset at every window start, frames keep their
+    global index (temporal position), and each window sees only its own
+    stored frames."""
+    wl = small_variants()["small_skip"]
+    cache = make_cache(wl)
+    run = Runner(wl, cache)
+    win = 7
+    for f in range(wl.frames):
+        if f % win == 0:
+            cache.reset(0)
+            orc = OracleStream(wl, lambda f_, t: qkv(wl, 0, 0, f_, t), window_start=f)
+        q, k, v = run.inputs(f)
+        run.frame(f, q, k, v, wl.is_keyframe(f))
+        torch.cuda.synchronize()
+        o, lse = orc.attend(f)
+        assert np.abs(run.out[0].float().cpu().numpy() - o).max() <= BF16_TOL, f
+        assert np.abs(run.lse[0].cpu().numpy() - lse).max() <= LSE_TOL, f
+
+
 def test_hip_graph_replays_follow_the_device_bookkeeping():
     """attend_frame captured once in a HIP graph (main kernel and split
     merge), then replayed after each eager append as the cache fills, evicts
