@@ -225,6 +225,28 @@ int kv_append_frame_grid(kv_handle* h, int layer, int frame_idx, int commit, int
                          const void* d_tables, void* stream);
 
 /*
+ * QKV projection fused with RoPE + append, bf16 caches only: the rotary
+ * embedding follows the Q/K projection and precedes the cache write
+ * ([ROPE-KV] FAQ on where RoPE is applied relative to the KV cache write).
+ * For every stream s, [Q | K | V] = x[s] w^T with fp32 accumulation, each
+ * product rounded once to bf16; then exactly kv_append_frame(h, layer,
+ * frame_idx, commit, Q, K, V, q_rot, d_tables) with the configured grid
+ * (same rounding, target page, frame record and pending commit), without
+ * Q, K and V ever being written to memory.
+ *   x:      [S][N][hidden] bf16, the frame's hidden states; read only
+ *   hidden: reduction length C, a multiple of 64 (>= 64)
+ *   w:      [3*H*D][hidden] bf16, the layer's projection as a linear layer
+ *           stores it (output channel major): rows 0 .. H*D-1 give Q (head h
+ *           at rows h*D ..), then K, then V; no bias; read only
+ *   q_rot:  output [S][N][H][D] bf16, as for kv_append_frame
+ * EINVAL for an fp32 cache, an odd num_heads, a hidden size that is not a
+ * positive multiple of 64, or a pointer that is null or not 16-byte aligned.
+ */
+int kv_project_append_frame(kv_handle* h, int layer, int frame_idx, int commit, const void* x,
+                            int hidden, const void* w, void* q_rot, const void* d_tables,
+                            void* stream);
+
+/*
  * Attention of the frame's N query tokens (all heads, all streams) over the
  * visible page table of `layer` ([ROPE-KV] "Attention Computation with Cached
  * RoPE"; [RT3D] "Per-Frame Processing and Causal Attention"):

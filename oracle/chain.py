@@ -27,6 +27,18 @@ from . import retained
 from . import rope3d
 
 
+def project_qkv(x, w, heads: int, head_dim: int, round_store: bool = True):
+    """The chain's projection of one frame: [Q | K | V] = store(store(x) @ w)
+    with x [N, C] and w [C, 3*H*D] (no bias), split into three [N, H, D]
+    arrays (head h at columns h*D .. h*D+D-1 of each third).  store() rounds
+    to bf16 when round_store is set (the stored projection output)."""
+    st = rope3d.round_bf16 if round_store else (lambda a: np.asarray(a, dtype=np.float64))
+    x = st(np.asarray(x, dtype=np.float64))
+    qkv = st(x @ np.asarray(w, dtype=np.float64))
+    n, hd = x.shape[0], heads * head_dim
+    return tuple(qkv[:, i * hd:(i + 1) * hd].reshape(n, heads, head_dim) for i in range(3))
+
+
 class OracleChain:
     def __init__(self, wl, x0: Callable[[int], np.ndarray], weight: Callable[[int], np.ndarray]):
         self.wl = wl
@@ -58,11 +70,7 @@ class OracleChain:
         x = np.asarray(self.x0(f), dtype=np.float64)
         outs: List[np.ndarray] = []
         for layer in range(wl.chain_layers):
-            xb = self._store(x)
-            qkv = self._store(xb @ self._weight(layer))
-            q = qkv[:, 0 * hid:1 * hid].reshape(n, h, d)
-            k = qkv[:, 1 * hid:2 * hid].reshape(n, h, d)
-            v = qkv[:, 2 * hid:3 * hid].reshape(n, h, d)
+            q, k, v = project_qkv(x, self._weight(layer), h, d, self.round)
             q = self._store(self._rotate(q, f))
             k = self._store(self._rotate(k, f))
             if layer % 2 == 0:

@@ -79,6 +79,13 @@ def kv_append_frame_grid(h, layer: int, frame_idx: int, commit: int, grid_h: int
            "kv_append_frame_grid")
 
 
+def kv_project_append_frame(h, layer: int, frame_idx: int, commit: int, x, hidden: int, w, q_rot,
+                            d_tables, stream: int) -> None:
+    _check(_lib.kv_project_append_frame(h, layer, frame_idx, int(commit), _vp(x), hidden, _vp(w),
+                                        _vp(q_rot), _vp(d_tables), stream),
+           "kv_project_append_frame")
+
+
 def attend_frame(h, layer: int, q_rot, out, lse, stream: int) -> None:
     _check(_lib.attend_frame(h, layer, _vp(q_rot), _vp(out), _vp(lse), stream), "attend_frame")
 
@@ -182,6 +189,11 @@ class PagedKVCache:
         else:
             kv_append_frame_grid(self.h, layer, frame_idx, commit, grid[0], grid[1], q, k, v,
                                  q_rot, self.tables, self.stream)
+
+    def project_append(self, layer, frame_idx, commit, x, w, q_rot):
+        """Fused projection + RoPE + append: x [S][N][hidden] bf16, w [3*H*D][hidden] bf16."""
+        kv_project_append_frame(self.h, layer, frame_idx, commit, x, x.shape[-1], w, q_rot,
+                                self.tables, self.stream)
 
     def attend(self, layer, q_rot, out, lse=None):
         attend_frame(self.h, layer, q_rot, out, lse, self.stream)

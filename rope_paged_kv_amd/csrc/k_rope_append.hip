@@ -27,106 +27,9 @@
 // bookkeeping never leaves the device: every workgroup derives the target page
 // from the state as it stands (which no workgroup of the launch modifies), and
 // one workgroup per stream writes the frame record -- no atomics, no fences.
-#include "rpkv_internal.h"
+#include "rope_rows.h"
 
 namespace rpkv {
-
-template <typename T>
-struct Vec;
-
-template <>
-struct Vec<uint16_t> {   // bf16 bit patterns
-    static constexpr int kCh = 8;
-    __device__ static inline void unpack(const uint4& r, float* f) {
-        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[2 * i] = __uint_as_float(w[i] << 16);
-            f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-        }
-    }
-    __device__ static inline uint32_t pack2(float lo, float hi) {
-        // round to nearest even (inputs are finite)
-        uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
-        a += 0x7FFFu + ((a >> 16) & 1u);
-        b += 0x7FFFu + ((b >> 16) & 1u);
-        return (a >> 16) | (b & 0xFFFF0000u);
-    }
-    __device__ static inline uint4 pack(const float* f) {
-        return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
-    }
-};
-
-template <>
-struct Vec<float> {
-    static constexpr int kCh = 4;
-    __device__ static inline void unpack(const uint4& r, float* f) {
-        f[0] = __uint_as_float(r.x);
-        f[1] = __uint_as_float(r.y);
-        f[2] = __uint_as_float(r.z);
-        f[3] = __uint_as_float(r.w);
-    }
-    __device__ static inline uint4 pack(const float* f) {
-        return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
-                          __float_as_uint(f[3]));
-    }
-};
-
-// Rotation coefficients (cos, sin) of pair j of a token at grid position
-// (hp, wp): the t table for j < pt, the h table for the next ph pairs and the
-// w table after that.
-__device__ inline float2 coeff(const AppendArgs& a, int j, int hp, int wp) {
-    const float2* src = j < a.pt ? a.tab_t + a.frame * a.pt + j
-                      : j < a.pt + a.ph ? a.tab_h + hp * a.ph + (j - a.pt)
-                                        : a.tab_w + wp * a.pw + (j - a.pt - a.ph);
-    return *src;
-}
-
-// Row and 16-byte chunk of a thread's chunk slot i.  Interleaved layout:
-// slots walk the tile's chunks in order.  Half-split layout: slots 2j and
-// 2j+1 are a pair of chunks that rotate together -- a chunk of the first half
-// of an axis block and the chunk pairs_a channels after it -- and the pair
-// slots walk the tile's first-half chunks in order (cpr/2 per row).
-template <int CH, int LAYOUT>
-__device__ inline void chunk_of(const AppendArgs& a, int tid, int i, int& r, int& c) {
-    constexpr int CPR = kHeadDim / CH;
-    if (LAYOUT == RPKV_ROPE_INTERLEAVED) {
-        const int id = tid + i * 256;
-        r = id / CPR;
-        c = id % CPR;
-        return;
-    }
-    const int id = tid + (i >> 1) * 256;
-    r = id / (CPR / 2);
-    int pc = id % (CPR / 2);
-    const int nt = a.pt / CH, nh = a.ph / CH, nw = a.pw / CH;   // first-half chunks per axis
-    int base, half;
-    if (pc < nt) {
-        base = 0;
-        half = nt;
-    } else if ((pc -= nt) < nh) {
-        base = 2 * nt;
-        half = nh;
-    } else {
-        pc -= nh;
-        base = 2 * (nt + nh);
-        half = nw;
-    }
-    c = base + pc + ((i & 1) ? half : 0);
-}
-
-// Rotation coefficients of a thread's chunk slots, flat: interleaved, pair e
-// of slot i at [i*CH/2 + e]; half-split, channel e of pair slot j at [j*CH + e].
-template <int CH, int LAYOUT>
-__device__ inline float2 coeff_of(const AppendArgs& a, int c, int e, int hp, int wp) {
-    if (LAYOUT == RPKV_ROPE_INTERLEAVED) return coeff(a, c * (CH / 2) + e, hp, wp);
-    // half-split: chunk c of the first half of its axis block; pair index
-    // inside the axis = channel offset from the block start.
-    const int nt = a.pt / CH, nh = a.ph / CH;
-    if (c < 2 * nt) return a.tab_t[a.frame * a.pt + c * CH + e];
-    if (c < 2 * (nt + nh)) return a.tab_h[hp * a.ph + (c - 2 * nt) * CH + e];
-    return a.tab_w[wp * a.pw + (c - 2 * (nt + nh)) * CH + e];
-}
 
 template <typename T, int LAYOUT>
 __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
@@ -185,15 +88,9 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
         }
     }
 
-    // Target of this append, from the state as it stands.
-    const int status = st->status;
-    const int n_free = st->n_free;
-    const int fresh = st->fresh;
-    const int page = n_free > 0 ? st->free_[n_free - 1] : fresh;
-    const int sp_off = st->n_sp;
-    // The special stream always has room for one frame beyond the committed
-    // ones; its capacity is checked when the frame is committed.
-    const bool ok = status == RPKV_OK && (n_free > 0 || fresh < a.pool);
+    const Target tg = append_target(a, st);
+    const int page = tg.page, sp_off = tg.sp_off;
+    const bool ok = tg.ok;
     T* kdst;
     if (special)
         kdst = (T*)a.ksp + s * a.ksp_elems + ((size_t)h * a.sp_cap + sp_off) * kHeadDim;
@@ -274,48 +171,8 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
         }
     }
 
-    // Frame record, written by one workgroup per stream: the visible table
-    // this frame's attention reads, and the pending commit that the deferred
-    // eviction call applies.  It touches only fields no workgroup of this
-    // launch reads (the structural state above is left as it is), so no
-    // workgroup waits for another.
-    if (tile != 0 || h != 0) return;
-    // Visible patch pages: scale pages, window oldest first, then the frame's
-    // own page (it comes last whether it will be committed or not).
-    const int ns = st->n_scale, nw = st->n_win, head = st->win_head;
-    const int vis_n = ok ? ns + nw + 1 : 0;
-    int full = 1;
-    for (int i = tid; i < vis_n; i += 256) {
-        const int pg = i < ns ? st->scale[i] : (i < ns + nw ? st->win[(head + i - ns) % kMaxPool] : page);
-        st->vis[i] = pg;
-        const int len = i < ns + nw ? st->page_tokens[pg] : a.fP;
-        st->vis_len[i] = len;
-        full &= len == a.P;
-    }
-    full = __syncthreads_and(full);
-    if (tid == 0) {
-        st->n_query = a.nsp + a.fP;
-        st->vis_full = full;
-        if (!ok) {
-            if (status == RPKV_OK) st->status = RPKV_ENOSPACE;
-            st->vis_n = 0;
-            st->vis_sp_tokens = 0;
-            st->vis_sp_pages = 0;
-            st->last_page_len = 0;
-            st->pending = 0;
-        } else {
-            const int vis_sp = sp_off + a.nsp;
-            const int sp_pages = (vis_sp + a.sp_page - 1) / a.sp_page;
-            st->target = page;
-            st->sp_off = sp_off;
-            st->page_tokens[page] = a.fP;
-            st->vis_n = vis_n;
-            st->vis_sp_tokens = vis_sp;
-            st->vis_sp_pages = sp_pages;
-            st->last_page_len = sp_pages ? vis_sp - (sp_pages - 1) * a.sp_page : 0;
-            st->pending = a.commit;
-        }
-    }
+    // Frame record, written by one workgroup per stream.
+    if (tile == 0 && h == 0) write_frame_record(a, st, tg, tid);
 }
 
 hipError_t launch_rope_append(const AppendArgs& a, int dtype, hipStream_t st) {

@@ -219,18 +219,11 @@ int kv_append_frame(kv_handle* h, int layer, int frame_idx, int commit, const vo
                                 q_rot, d_tables, stream);
 }
 
-int kv_append_frame_grid(kv_handle* h, int layer, int frame_idx, int commit, int grid_h,
-                         int grid_w, const void* q, const void* k, const void* v, void* q_rot,
-                         const void* d_tables, void* stream) {
-    if (!h || layer < 0 || layer >= h->cfg.num_layers) return RPKV_EINVAL;
-    if (frame_idx < 0 || frame_idx >= h->cfg.rope.max_frames || (commit != 0 && commit != 1))
-        return RPKV_EINVAL;
-    if (grid_h < 1 || grid_w < 1 || grid_h > h->cfg.rope.max_h || grid_w > h->cfg.rope.max_w ||
-        (long long)grid_h * grid_w > h->L.P)
-        return RPKV_EINVAL;
-    if (!q || !k || !v || !q_rot || !d_tables) return RPKV_EINVAL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_rot) || !aligned16(d_tables))
-        return RPKV_EINVAL;
+// Append arguments of one frame of `layer` (shared by the plain and the fused
+// append).
+static AppendArgs append_args(kv_handle* h, int layer, int frame_idx, int commit, int grid_h,
+                              int grid_w, const void* q, const void* k, const void* v,
+                              void* q_rot, const void* d_tables) {
     const Layout& L = h->L;
     const rope3d_spec& r = h->cfg.rope;
     AppendArgs a;
@@ -270,7 +263,49 @@ int kv_append_frame_grid(kv_handle* h, int layer, int frame_idx, int commit, int
     a.frame = frame_idx;
     a.commit = commit;
     a.n_tiles = 1 + L.tpp;
+    return a;
+}
+
+int kv_append_frame_grid(kv_handle* h, int layer, int frame_idx, int commit, int grid_h,
+                         int grid_w, const void* q, const void* k, const void* v, void* q_rot,
+                         const void* d_tables, void* stream) {
+    if (!h || layer < 0 || layer >= h->cfg.num_layers) return RPKV_EINVAL;
+    if (frame_idx < 0 || frame_idx >= h->cfg.rope.max_frames || (commit != 0 && commit != 1))
+        return RPKV_EINVAL;
+    if (grid_h < 1 || grid_w < 1 || grid_h > h->cfg.rope.max_h || grid_w > h->cfg.rope.max_w ||
+        (long long)grid_h * grid_w > h->L.P)
+        return RPKV_EINVAL;
+    if (!q || !k || !v || !q_rot || !d_tables) return RPKV_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_rot) || !aligned16(d_tables))
+        return RPKV_EINVAL;
+    AppendArgs a = append_args(h, layer, frame_idx, commit, grid_h, grid_w, q, k, v, q_rot, d_tables);
     const int rc = hip_status(launch_rope_append(a, h->cfg.dtype, (hipStream_t)stream));
+    if (rc == RPKV_OK && layer == 0) {
+        h->appended++;
+        h->committed += commit;
+    }
+    return rc;
+}
+
+int kv_project_append_frame(kv_handle* h, int layer, int frame_idx, int commit, const void* x,
+                            int hidden, const void* w, void* q_rot, const void* d_tables,
+                            void* stream) {
+    if (!h || layer < 0 || layer >= h->cfg.num_layers) return RPKV_EINVAL;
+    if (h->cfg.dtype != RPKV_BF16 || h->L.H % 2 != 0) return RPKV_EINVAL;
+    if (frame_idx < 0 || frame_idx >= h->cfg.rope.max_frames || (commit != 0 && commit != 1))
+        return RPKV_EINVAL;
+    if (hidden < 64 || hidden % 64 != 0) return RPKV_EINVAL;
+    if (!x || !w || !q_rot || !d_tables) return RPKV_EINVAL;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(q_rot) || !aligned16(d_tables)) return RPKV_EINVAL;
+    ProjArgs p;
+    p.a = append_args(h, layer, frame_idx, commit, h->cfg.grid_h, h->cfg.grid_w, nullptr, nullptr,
+                      nullptr, q_rot, d_tables);
+    p.x = (const uint16_t*)x;
+    p.w = (const uint16_t*)w;
+    p.C = hidden;
+    p.row_blocks = (p.a.fP + p.a.nsp + 127) / 128;
+    p.col_blocks = 3 * h->L.H * kHeadDim / 128;
+    const int rc = hip_status(launch_project_append(p, (hipStream_t)stream));
     if (rc == RPKV_OK && layer == 0) {
         h->appended++;
         h->committed += commit;

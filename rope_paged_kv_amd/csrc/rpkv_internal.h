@@ -84,6 +84,17 @@ struct AppendArgs {
     int n_tiles;            // workgroups per (stream, head)
 };
 
+// The fused projection + append: the append's arguments (q, k, v unused)
+// plus the projection operands.
+struct ProjArgs {
+    AppendArgs a;
+    const uint16_t* x;      // [S][N][C] bf16
+    const uint16_t* w;      // [3*H*D][C] bf16
+    int C;
+    int row_blocks;         // 128-row tiles of the frame's tokens
+    int col_blocks;         // 128-channel tiles of the 3*H*D outputs
+};
+
 struct AttnArgs {
     const void* q;          // q_rot [S][N][H][D]
     void* out;              // [S][N][H][D]
@@ -109,6 +120,7 @@ hipError_t launch_evict(CacheState* states, int count, int scale_frames, int sli
                         int max_sp_tokens, int nsp, hipStream_t st);
 hipError_t launch_rollback(CacheState* states, int count, hipStream_t st);
 hipError_t launch_rope_append(const AppendArgs& a, int dtype, hipStream_t st);
+hipError_t launch_project_append(const ProjArgs& p, hipStream_t st);
 hipError_t launch_attend(const AttnArgs& a, int dtype, hipStream_t st);
 hipError_t launch_attend_bf16_main(const AttnArgs& a, hipStream_t st);
 

@@ -144,6 +144,15 @@ def small_variants() -> dict:
         # NTK-stretched base
         "small_ntk": Workload("small_ntk_8x8", "bf16", frames=6, grid_h=8, grid_w=8, heads=2,
                               scale_frames=1, sliding_window=2, keyframe_interval=1, ntk_factor=4.0),
+        # fused projection + append: 13x17 (the specials share the last row
+        # tile with the patches), hidden = H*D; 5x25 half-split (the specials
+        # straddle two row tiles), hidden 192 != H*D
+        "small_proj": Workload("small_proj_13x17", "bf16", frames=6, grid_h=13, grid_w=17, heads=4,
+                               streams=2, scale_frames=1, sliding_window=2, keyframe_interval=2,
+                               hidden=256),
+        "small_proj_half": Workload("small_proj_half_5x25", "bf16", frames=5, grid_h=5, grid_w=25,
+                                    heads=2, scale_frames=1, sliding_window=2, keyframe_interval=1,
+                                    pairs=(0, 16, 16), theta=100.0, rope_layout=1, hidden=192),
         # frames of their own patch grids, up to 9x11 (partial patch pages)
         "small_vargrid": Workload("small_vargrid_9x11", "bf16", frames=10, grid_h=9, grid_w=11,
                                   heads=3, scale_frames=2, sliding_window=3, keyframe_interval=1,
@@ -208,11 +217,11 @@ def embeddings(wl: Workload, stream: int, frame: int) -> np.ndarray:
         (wl.tokens, wl.hidden), dtype=np.float32)
 
 
-def projection(wl: Workload, layer: int) -> np.ndarray:
-    """QKV projection of one chain layer: float32 [hidden, 3*hidden], N(0, 0.02),
-    rounded to the storage dtype."""
+def projection(wl: Workload, layer: int, n_out: Optional[int] = None) -> np.ndarray:
+    """QKV projection of one chain layer: float32 [hidden, n_out] (default
+    3*hidden), N(0, 0.02), rounded to the storage dtype."""
     w = _rng(wl, layer, 0, 0, TENSOR_W).standard_normal(
-        (wl.hidden, 3 * wl.hidden), dtype=np.float32) * np.float32(0.02)
+        (wl.hidden, n_out or 3 * wl.hidden), dtype=np.float32) * np.float32(0.02)
     return _store(wl, w)
 
 

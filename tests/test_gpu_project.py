@@ -1,0 +1,109 @@
+"""GPU parity of the fused projection + RoPE + append (kv_project_append_frame)
+against the float64 oracle: the chain's projection (oracle.chain.project_qkv)
+feeding the oracle stream's rotation, pages and attention.
+
+Inputs: the chain's seeded hidden states N(0, 1) and projection weights
+N(0, 0.02), both bf16; with these widths the projections stay below 2 in
+magnitude, so a one-ulp difference in the stored projection (fp32 vs exact
+accumulation landing on the other side of a bf16 rounding boundary) plus the
+final rounding stays under the 2e-2 bar."""
+import numpy as np
+import pytest
+import torch
+
+import rope_paged_kv_amd as rp
+from gpu_harness import make_cache, to_dev
+from oracle import pages, rope3d
+from oracle.chain import project_qkv
+from oracle.stream import OracleStream
+from rpkv_inputs import embeddings, projection, small_variants
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+LSE_TOL = 1e-2
+
+
+def _views(cache, s):
+    kp, vp, ks, vs = cache.pool_views()
+    return kp[0, s], vp[0, s], ks[0, s], vs[0, s]
+
+
+@pytest.mark.parametrize("name", ["small_proj", "small_proj_half"])
+def test_project_append_matches_oracle(name):
+    wl = small_variants()[name]
+    S, H, D, C, N, P, ns = wl.streams, wl.heads, wl.head_dim, wl.hidden, wl.tokens, wl.patches, wl.n_special
+    cache = make_cache(wl)
+    sim = pages.PageSim(wl.scale_frames, wl.sliding_window, wl.special_page_size, wl.n_special)
+    w = projection(wl, 0, n_out=3 * H * D)                    # [C, 3*H*D]
+    w_dev = to_dev(w.T, torch.bfloat16)                       # linear-layer layout [3*H*D][C]
+    proj = {}
+
+    def source(s):
+        def get(f, t):
+            if (s, f) not in proj:
+                proj[(s, f)] = project_qkv(embeddings(wl, s, f), w, H, D)
+            return proj[(s, f)][t]
+        return get
+
+    orc = {s: OracleStream(wl, source(s)) for s in range(S)}
+    shape = (S, N, H, D)
+    q_rot = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((S, H, N), dtype=torch.float32, device="cuda")
+    perm = np.array([rp.vslot_perm(p) for p in range(64)])
+    for f in range(wl.frames):
+        commit = wl.is_keyframe(f)
+        x = np.stack([embeddings(wl, s, f) for s in range(S)])
+        cache.project_append(0, f, int(commit), to_dev(x, torch.bfloat16), w_dev, q_rot)
+        sim.append(f, commit)
+        cache.attend(0, q_rot, out, lse)
+        torch.cuda.synchronize()
+        for s in range(S):
+            st = cache.state(0, s)
+            assert st["target_page"] == sim.target and st["special_offset"] == sim.sp_offset, (f, s)
+            assert st["visible_pages"] == sim.visible.patch_pages, (f, s)
+            assert st["visible_special_tokens"] == sim.visible.special_tokens, (f, s)
+            assert st["query_tokens"] == N and st["page_tokens"][sim.target] == P, (f, s)
+            want_q = orc[s].q_rot(f)
+            assert np.abs(q_rot[s].float().cpu().numpy() - want_q).max() <= BF16_TOL, (f, s)
+            want_k, want_v = orc[s].kv(f)
+            kp, vp, ks, vs = _views(cache, s)
+            t, o = sim.target, sim.sp_offset
+            got_k = kp[:, t, :P].float().cpu().numpy().transpose(1, 0, 2)
+            assert np.abs(got_k - want_k[ns:]).max() <= BF16_TOL, (f, s)
+            got_ks = ks[:, o:o + ns].float().cpu().numpy().transpose(1, 0, 2)
+            assert np.abs(got_ks - want_k[:ns]).max() <= BF16_TOL, (f, s)
+            vt = vp[:, t].float().cpu().numpy()               # [H][D][cap]
+            cap = vt.shape[-1]
+            key_of_pos = (np.arange(cap) // 64) * 64 + perm[np.arange(cap) % 64]
+            by_key = vt[:, :, np.argsort(key_of_pos)]
+            assert np.abs(by_key[:, :, :P].transpose(2, 0, 1) - want_v[ns:]).max() <= BF16_TOL, (f, s)
+            # the padding slots of the last written tile are zeros
+            assert np.all(by_key[:, :, P:(P + 63) // 64 * 64] == 0), (f, s)
+            spos = [(j // 64) * 64 + perm[j % 64] for j in range(o, o + ns)]
+            got_vs = vs[:, :, spos].float().cpu().numpy().transpose(2, 0, 1)
+            assert np.abs(got_vs - want_v[:ns]).max() <= BF16_TOL, (f, s)
+            o_want, lse_want = orc[s].attend(f)
+            assert np.abs(out[s].float().cpu().numpy() - o_want).max() <= BF16_TOL, (f, s)
+            assert np.abs(lse[s].cpu().numpy() - lse_want).max() <= LSE_TOL, (f, s)
+        sim.evict()
+        cache.evict(0)
+
+
+def test_project_append_checks_its_arguments():
+    wl = small_variants()["small_proj"]
+    cache = make_cache(wl)
+    H, D, C, N = wl.heads, wl.head_dim, wl.hidden, wl.tokens
+    x = torch.zeros((wl.streams, N, C), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((3 * H * D, C), dtype=torch.bfloat16, device="cuda")
+    q_rot = torch.empty((wl.streams, N, H, D), dtype=torch.bfloat16, device="cuda")
+    for hidden in (0, 32, 96):
+        with pytest.raises(rp.RpkvError):
+            rp.kv_project_append_frame(cache.h, 0, 0, 1, x, hidden, w, q_rot, cache.tables, cache.stream)
+    odd = make_cache(small_variants()["small_skip"])          # 3 heads
+    with pytest.raises(rp.RpkvError):
+        rp.kv_project_append_frame(odd.h, 0, 0, 1, x, C, w, q_rot, odd.tables, odd.stream)
+    f32 = make_cache(small_variants()["small_f32"])
+    with pytest.raises(rp.RpkvError):
+        rp.kv_project_append_frame(f32.h, 0, 0, 1, x, C, w, q_rot, f32.tables, f32.stream)
