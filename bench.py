@@ -9,8 +9,8 @@ workload is the single-layer bf16 stream of 64 frames of 37x37 patches + 6
 special tokens, 16 heads of 64, scale_frames 8, sliding_window 16, every frame
 a keyframe.  --workload 0/2/3 select the other single-layer streams, --workload
 4 the full-depth stack (4 streams x 24 layers alternating frame and global
-attention, QKV projection GEMMs and fp32 residual included; value counts
-stream-frames).  All inputs are generated (seeded, N(0,1), rounded to bf16)
+attention, the fused QKV projection + RoPE + append (kv_project_append_frame)
+and the fp32 residual included; value counts stream-frames).  All inputs are generated (seeded, N(0,1), rounded to bf16)
 and copied to HBM before timing.
 
 Prints one JSON line: value = frames/s over the K timed steps; roofline of the
@@ -286,7 +286,7 @@ def bench_full_depth(wl, args, dev):
     res = result_line(wl, args, elapsed, F * wl.streams, att_ms, flops, None,
                       fds.global_cache.info()["attn_splits"], unit="stream-frames/s", extra=extra,
                       config_extra={"layers": wl.chain_layers, "hidden": wl.hidden,
-                                    "includes": "QKV projection GEMMs and residual"})
+                                    "includes": "fused QKV projection + RoPE + append, residual"})
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle chain on a sample")
         res["cpu_baseline"] = cpu_baseline_chain(wl)

@@ -3,13 +3,14 @@ layers (attention over the frame's own tokens, nothing retained) and global
 layers (attention over the dual-stream paged cache), for several independent
 streams batched in every call.
 
-Per layer: [Q | K | V] = bf16(x) @ W_l (torch GEMM: the projection is the
-model's, not part of the hot path), then the library's RoPE + append,
-attention and (global layers) deferred eviction, then the residual
-x <- x + O in fp32.  Frame and global blocks are named on page "How
-LingBot-Map Achieves Real-Time 3D Reconstruction", section "AggregatorStream
-with FlashInfer Paged KV Cache"; the block internals need trained weights,
-so this driver keeps only the projection, the attention and the residual.
+Per layer: the library's fused projection + RoPE + append
+(kv_project_append_frame: [Q | K | V] = bf16(x) W_l^T on the matrix cores,
+rotated and written straight to q_rot and the pages), attention and (global
+layers) deferred eviction, then the residual x <- x + O in fp32.  Frame and
+global blocks are named on page "How LingBot-Map Achieves Real-Time 3D
+Reconstruction", section "AggregatorStream with FlashInfer Paged KV Cache";
+the block internals need trained weights, so this driver keeps only the
+projection, the attention and the residual.
 """
 from __future__ import annotations
 
@@ -48,13 +49,13 @@ class FullDepthStream:
                                                      sliding_window=sliding_window,
                                                      max_keyframes=n_kf, attn_splits=attn_splits,
                                                      **common), device=self.device)
-        # W_l split into its Q, K, V thirds (contiguous, so each GEMM writes a
-        # contiguous [S*N, H*D] = [S][N][H][D] tensor).
-        self.w = [tuple(wl[:, i * self.hidden:(i + 1) * self.hidden].contiguous() for i in range(3))
-                  for wl in weights]
+        # W_l [hidden, 3*hidden] (x @ W_l) stored transposed, output channel
+        # major as a linear layer keeps it: the fused kernel's layout.
+        self.w = [wl.t().contiguous() for wl in weights]
+        self.xb = torch.empty((streams, self.N, self.hidden), dtype=torch.bfloat16, device=self.device)
         shape = (streams, self.N, heads, head_dim)
         mk = lambda: torch.empty(shape, dtype=torch.bfloat16, device=self.device)
-        self.q, self.k, self.v, self.q_rot, self.out = mk(), mk(), mk(), mk(), mk()
+        self.q_rot, self.out = mk(), mk()
 
     def reset(self):
         self.global_cache.reset(-1)
@@ -66,16 +67,11 @@ class FullDepthStream:
         layers; appends each layer's attention output to `keep` if given, and
         (frame, layer, start event, end event) around each attention launch to
         `events` if given."""
-        rows = self.S * self.N
         commit = int(f % self.interval == 0)
         for layer in range(self.L):
-            xb = x.view(rows, self.hidden).to(torch.bfloat16)
-            wq, wk, wv = self.w[layer]
-            torch.mm(xb, wq, out=self.q.view(rows, self.hidden))
-            torch.mm(xb, wk, out=self.k.view(rows, self.hidden))
-            torch.mm(xb, wv, out=self.v.view(rows, self.hidden))
+            self.xb.copy_(x)
             c, g, cm = (self.frame_cache, 0, 0) if layer % 2 == 0 else (self.global_cache, layer // 2, commit)
-            c.append(g, f, cm, self.q, self.k, self.v, self.q_rot)
+            c.project_append(g, f, cm, self.xb, self.w[layer], self.q_rot)
             if events is not None:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()

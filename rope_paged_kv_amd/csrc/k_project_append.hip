@@ -50,8 +50,11 @@ constexpr int kOpBytes = 128 * kPK * 2;        // one operand tile of a stage: 1
 constexpr int kStageBytes = 2 * kOpBytes;      // W tile then X tile
 constexpr int kPitch = kHeadDim + 8;           // staging row pitch in elements (144 B)
 
-// Byte offset of 16-byte chunk c (of 8) of row r in an operand tile.
-__device__ inline int op_off(int r, int c) { return r * (kPK * 2) + ((c ^ (r & 7)) << 4); }
+// Byte offset of 16-byte chunk c (of 8) of row r in an operand tile.  A
+// 128-byte row covers half of the 64 LDS banks, so 16 consecutive rows (the
+// lanes an operand read serves together) reach every bank group once when
+// chunk c of row r sits at position c ^ ((r >> 1) & 7).
+__device__ inline int op_off(int r, int c) { return r * (kPK * 2) + ((c ^ ((r >> 1) & 7)) << 4); }
 
 __device__ inline uint16_t bf16_rne(float x) {   // finite input
     uint32_t u = __float_as_uint(x);
@@ -116,23 +119,22 @@ __global__ __launch_bounds__(256, 2) void k_project_append(ProjArgs p) {
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     const int nk = p.C / kPK;
+    const int arow = 64 * wo + (lane & 31), brow = 64 * wv + (lane & 31), khalf = lane >> 5;
     PROJ_GLOAD(0)
     PROJ_LSTORE(0)
     __syncthreads();
-    const int arow = 64 * wo + (lane & 31), brow = 64 * wv + (lane & 31), khalf = lane >> 5;
     for (int kt = 0; kt < nk; ++kt) {
         if (kt + 1 < nk) {
             PROJ_GLOAD((kt + 1) * kPK)
         }
         const char* A = lds + (kt & 1) * kStageBytes;
-        const char* B = A + kOpBytes;
 #pragma unroll
         for (int ks = 0; ks < kPK / 16; ++ks) {
             bf16x8 af[2], bf[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 af[j] = *(const bf16x8*)(A + op_off(arow + 32 * j, 2 * ks + khalf));
-                bf[j] = *(const bf16x8*)(B + op_off(brow + 32 * j, 2 * ks + khalf));
+                bf[j] = *(const bf16x8*)(A + kOpBytes + op_off(brow + 32 * j, 2 * ks + khalf));
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -145,7 +147,6 @@ __global__ __launch_bounds__(256, 2) void k_project_append(ProjArgs p) {
         }
         __syncthreads();
     }
-
 #undef PROJ_GLOAD
 #undef PROJ_LSTORE
 
@@ -159,6 +160,29 @@ __global__ __launch_bounds__(256, 2) void k_project_append(ProjArgs p) {
     CacheState* st = a.states + s;
     const Target tg = append_target(a, st);
     uint16_t* stg = (uint16_t*)lds + wave * (64 * kPitch);      // this wave's 64 x 72 staging tile
+
+    // Q and K: this lane rotates NSLOT chunk slots (interleaved: chunk lane % 8
+    // of rows lane / 8 + 8 i; half-split: pair slot lane % 4 of rows lane / 4
+    // + 16 i).  Their rotation coefficients are loaded first, so that the
+    // loads are in flight while the products are staged.
+    constexpr bool kInter = LAYOUT == RPKV_ROPE_INTERLEAVED;
+    constexpr int NSLOT = kInter ? 8 : 4, NCO = kInter ? 4 : 8;
+    float2 cw[NSLOT][NCO];
+    if (part < 2) {
+#pragma unroll
+        for (int i = 0; i < NSLOT; ++i) {
+            const int row = kInter ? (lane >> 3) + 8 * i : (lane >> 2) + 16 * i;
+            const int c = kInter ? (lane & 7) : pair_chunk<8>(a, lane & 3, 0);
+            const int V = V0 + row;
+            int hp = 0, wp = 0;   // specials (and rows past the frame) sit at h = w = 0
+            if (V < a.fP) {
+                hp = V / a.fgw;
+                wp = V - hp * a.fgw;
+            }
+#pragma unroll
+            for (int e = 0; e < NCO; ++e) cw[i][e] = coeff_of<8, LAYOUT>(a, c, e, hp, wp);
+        }
+    }
 
     if (part < 2) {
         // token-major: stg[row][channel]
@@ -203,31 +227,25 @@ __global__ __launch_bounds__(256, 2) void k_project_append(ProjArgs p) {
                           ((size_t)head * a.pool + tg.page) * a.slot_cap * kHeadDim;
         uint16_t* kspb = (uint16_t*)a.ksp + s * a.ksp_elems + ((size_t)head * a.sp_cap + tg.sp_off) * kHeadDim;
         // Destination of row `row` of this wave (null: nothing to write).
-        auto dst_row = [&](int row, int& hp, int& wp) -> uint16_t* {
+        auto dst_row = [&](int row) -> uint16_t* {
             const int V = V0 + row;
-            hp = wp = 0;   // specials sit at h = w = 0
             if (V >= nvalid) return nullptr;
             const bool patch = V < a.fP;
-            if (patch) {
-                hp = V / a.fgw;
-                wp = V - hp * a.fgw;
-            }
             if (part == 0) return qdst + (size_t)(patch ? a.nsp + V : V - a.fP) * rs;
             if (!tg.ok) return nullptr;
             return patch ? kpage + (size_t)V * kHeadDim : kspb + (size_t)(V - a.fP) * kHeadDim;
         };
-        if (LAYOUT == RPKV_ROPE_INTERLEAVED) {
+        if (kInter) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int id = lane + 64 * i, row = id >> 3, c = id & 7;
-                int hp, wp;
-                uint16_t* d = dst_row(row, hp, wp);
+            for (int i = 0; i < NSLOT; ++i) {
+                const int row = (lane >> 3) + 8 * i, c = lane & 7;
+                uint16_t* d = dst_row(row);
                 if (!d) continue;
                 float f[8];
                 Vec<uint16_t>::unpack(*(const uint4*)(stg + row * kPitch + c * 8), f);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float2 w = coeff_of<8, LAYOUT>(a, c, e, hp, wp);
+                    const float2 w = cw[i][e];
                     const float x = f[2 * e], y = f[2 * e + 1];
                     f[2 * e] = x * w.x - y * w.y;
                     f[2 * e + 1] = x * w.y + y * w.x;
@@ -235,19 +253,18 @@ __global__ __launch_bounds__(256, 2) void k_project_append(ProjArgs p) {
                 *(uint4*)(d + c * 8) = Vec<uint16_t>::pack(f);
             }
         } else {
+            const int c0 = pair_chunk<8>(a, lane & 3, 0), c1 = pair_chunk<8>(a, lane & 3, 1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int id = lane + 64 * i, row = id >> 2, pc = id & 3;
-                int hp, wp;
-                uint16_t* d = dst_row(row, hp, wp);
+            for (int i = 0; i < NSLOT; ++i) {
+                const int row = (lane >> 2) + 16 * i;
+                uint16_t* d = dst_row(row);
                 if (!d) continue;
-                const int c0 = pair_chunk<8>(a, pc, 0), c1 = pair_chunk<8>(a, pc, 1);
                 float f0[8], f1[8];
                 Vec<uint16_t>::unpack(*(const uint4*)(stg + row * kPitch + c0 * 8), f0);
                 Vec<uint16_t>::unpack(*(const uint4*)(stg + row * kPitch + c1 * 8), f1);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float2 w = coeff_of<8, LAYOUT>(a, c0, e, hp, wp);
+                    const float2 w = cw[i][e];
                     const float x = f0[e], y = f1[e];
                     f0[e] = x * w.x - y * w.y;
                     f1[e] = y * w.x + x * w.y;
