@@ -26,7 +26,8 @@
 // (the layout the attention kernel's matrix-core operands read).  The
 // bookkeeping never leaves the device: every workgroup derives the target page
 // from the state as it stands (which no workgroup of the launch modifies), and
-// one workgroup per stream writes the frame record -- no atomics, no fences.
+// one extra workgroup per stream, the first of its row of the grid, writes the
+// frame record -- no atomics, no fences.
 #include "rope_rows.h"
 
 namespace rpkv {
@@ -39,8 +40,16 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
     constexpr int PER = NCH / 256;         // chunks per thread
     __shared__ T vt[kHeadDim][kTile + CH]; // V^T of the tile: row d, storage position
 
-    const int tile = blockIdx.x, h = blockIdx.y, s = blockIdx.z, tid = threadIdx.x;
+    const int h = blockIdx.y, s = blockIdx.z, tid = threadIdx.x;
     CacheState* st = a.states + s;
+    // Workgroup x = 0 of head 0 writes the frame record and nothing else, so
+    // its chain of dependent bookkeeping loads starts with the launch instead
+    // of trailing a tile's work; x = 0 of the other heads has nothing to do.
+    if (blockIdx.x == 0) {
+        if (h == 0) write_frame_record(a, st, append_target(a, st), tid);
+        return;
+    }
+    const int tile = blockIdx.x - 1;
 
     const bool special = tile == 0;
     const int slot0 = special ? 0 : (tile - 1) * kTile;
@@ -170,13 +179,10 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
             }
         }
     }
-
-    // Frame record, written by one workgroup per stream.
-    if (tile == 0 && h == 0) write_frame_record(a, st, tg, tid);
 }
 
 hipError_t launch_rope_append(const AppendArgs& a, int dtype, hipStream_t st) {
-    dim3 grid(a.n_tiles, a.H, a.S);
+    dim3 grid(a.n_tiles + 1, a.H, a.S);   // x = 0: the frame record
     const bool half = a.layout == RPKV_ROPE_HALF_SPLIT;
     if (dtype == RPKV_BF16) {
         if (half)
