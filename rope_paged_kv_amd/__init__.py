@@ -153,6 +153,8 @@ class PagedKVCache:
         self.torch = torch
         self.cfg = cfg
         self.device = torch.device(device)
+        if self.device.index is None:   # "cuda" -> the current device, as tensors report it
+            self.device = torch.device(self.device.type, torch.cuda.current_device())
         nbytes = kv_required_bytes(cfg)
         if nbytes == 0:
             raise RpkvError(RPKV_EINVAL, "kv_required_bytes")
@@ -166,6 +168,24 @@ class PagedKVCache:
     @property
     def stream(self) -> int:
         return self.torch.cuda.current_stream(self.device).cuda_stream
+
+    def _expect(self, name, t, shape, dtype):
+        """The C ABI takes bare pointers: check a torch tensor's shape, dtype,
+        device and layout here, before anything is launched (raw integer
+        pointers are passed through unchecked)."""
+        if t is None or isinstance(t, int):
+            return
+        if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != self.device \
+                or not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous {dtype} tensor of shape {tuple(shape)} "
+                             f"on {self.device}, got {t.dtype} {tuple(t.shape)} on {t.device}"
+                             f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+
+    def _act(self, name, t, rows=None):
+        c = self.cfg
+        dt = self.torch.bfloat16 if c.dtype == RPKV_BF16 else self.torch.float32
+        n = c.special_tokens + c.grid_h * c.grid_w
+        self._expect(name, t, (c.num_streams, n, c.num_heads, c.head_dim), dt)
 
     def close(self):
         if getattr(self, "h", None) is not None:
@@ -183,6 +203,8 @@ class PagedKVCache:
 
     def append(self, layer, frame_idx, commit, q, k, v, q_rot, grid=None):
         """grid: this frame's (grid_h, grid_w) if it differs from the configured one."""
+        for name, t in (("q", q), ("k", k), ("v", v), ("q_rot", q_rot)):
+            self._act(name, t)
         if grid is None:
             kv_append_frame(self.h, layer, frame_idx, commit, q, k, v, q_rot, self.tables,
                             self.stream)
@@ -192,10 +214,21 @@ class PagedKVCache:
 
     def project_append(self, layer, frame_idx, commit, x, w, q_rot):
         """Fused projection + RoPE + append: x [S][N][hidden] bf16, w [3*H*D][hidden] bf16."""
+        c, bf = self.cfg, self.torch.bfloat16
+        n = c.special_tokens + c.grid_h * c.grid_w
+        hidden = x.shape[-1]
+        self._expect("x", x, (c.num_streams, n, hidden), bf)
+        self._expect("w", w, (3 * c.num_heads * c.head_dim, hidden), bf)
+        self._act("q_rot", q_rot)
         kv_project_append_frame(self.h, layer, frame_idx, commit, x, x.shape[-1], w, q_rot,
                                 self.tables, self.stream)
 
     def attend(self, layer, q_rot, out, lse=None):
+        self._act("q_rot", q_rot)
+        self._act("out", out)
+        c = self.cfg
+        self._expect("lse", lse, (c.num_streams, c.num_heads, c.special_tokens + c.grid_h * c.grid_w),
+                     self.torch.float32)
         attend_frame(self.h, layer, q_rot, out, lse, self.stream)
 
     def evict(self, layer):

@@ -490,3 +490,26 @@ def test_replay_is_bitwise_deterministic():
             acc.append(run.out.clone())
         outs.append(torch.stack(acc))
     assert torch.equal(outs[0], outs[1])
+
+
+def test_binding_checks_tensor_shapes_before_launch():
+    """The C ABI takes bare pointers; the torch convenience layer refuses a
+    tensor of the wrong shape, dtype or layout before anything is launched."""
+    wl = small_variants()["small_bf16"]
+    cache = make_cache(wl)
+    run = Runner(wl, cache)
+    q, k, v = run.inputs(0)
+    with pytest.raises(ValueError):
+        cache.append(0, 0, 1, q[:, :-1], k, v, run.q_rot)
+    with pytest.raises(ValueError):
+        cache.append(0, 0, 1, q.float(), k, v, run.q_rot)
+    with pytest.raises(ValueError):
+        cache.append(0, 0, 1, q.transpose(1, 2).contiguous().transpose(1, 2), k, v, run.q_rot)
+    with pytest.raises(ValueError):
+        cache.attend(0, run.q_rot, run.out, run.lse[:, :, :-1])
+    st = cache.state(0, 0)
+    assert st["query_tokens"] == 0 and st["n_visible_pages"] == 0   # nothing ran
+    cache.append(0, 0, 1, q, k, v, run.q_rot)
+    cache.attend(0, run.q_rot, run.out, run.lse)
+    torch.cuda.synchronize()
+    assert cache.state(0, 0)["query_tokens"] == wl.tokens
