@@ -513,3 +513,37 @@ def test_binding_checks_tensor_shapes_before_launch():
     cache.attend(0, run.q_rot, run.out, run.lse)
     torch.cuda.synchronize()
     assert cache.state(0, 0)["query_tokens"] == wl.tokens
+
+
+def test_maximum_pool_of_512_pages():
+    """The largest pool a cache takes (scale_frames + sliding_window + 1 = 512
+    pages): the window fills to 509 pages, the visible table reaches 512
+    entries (two passes of the frame record's 256 threads, 512 one-tile pages
+    of 6 keys each in the attention walk) and pages recycle; bookkeeping
+    bit-exact against the page simulator, attention against the oracle.  A
+    513-page pool is refused."""
+    from rpkv_inputs import Workload
+    wl = Workload("max_pool_2x3", "bf16", frames=530, grid_h=2, grid_w=3, heads=2,
+                  scale_frames=2, sliding_window=509, keyframe_interval=1)
+    cache = make_cache(wl)
+    run = Runner(wl, cache)
+    sim = sim_for(wl)
+    orc = OracleStream(wl, lambda f, t: qkv(wl, 0, 0, f, t))
+    check = {0, 255, 256, 300, 510, 511, 512, 529}
+    for f in range(wl.frames):
+        q, k, v = run.inputs(f)
+        sim.append(f, True)
+        run.frame(f, q, k, v, True, evict=False)
+        if f in check:
+            st = cache.state(0, 0)
+            check_state(st, sim, f)
+            assert len(st["visible_pages"]) == min(f + 1, 512), f
+            torch.cuda.synchronize()
+            o, lse = orc.attend(f)
+            assert np.abs(run.out[0].float().cpu().numpy() - o).max() <= BF16_TOL, f
+            assert np.abs(run.lse[0].cpu().numpy() - lse).max() <= LSE_TOL, f
+        sim.evict()
+        cache.evict(0)
+    check_after_evict(cache.state(0, 0), sim, wl.frames)
+    with pytest.raises(rp.RpkvError):
+        make_cache(wl.replace(sliding_window=510))
