@@ -107,3 +107,39 @@ def test_project_append_checks_its_arguments():
     f32 = make_cache(small_variants()["small_f32"])
     with pytest.raises(rp.RpkvError):
         rp.kv_project_append_frame(f32.h, 0, 0, 1, x, C, w, q_rot, f32.tables, f32.stream)
+
+
+def test_project_append_shares_the_overflow_rule():
+    """The fused path takes the same append target and frame record as
+    kv_append_frame: a keyframe past max_keyframes sets the sticky
+    ENOSPACE, later fused appends write nothing to the pages and show an empty
+    visible set (attention: zeros, lse -inf), and a reset recovers."""
+    wl = small_variants()["small_proj"]
+    S, H, D, C, N = wl.streams, wl.heads, wl.head_dim, wl.hidden, wl.tokens
+    cache = make_cache(wl, max_keyframes=2)
+    x = torch.zeros((S, N, C), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((3 * H * D, C), dtype=torch.bfloat16, device="cuda")
+    q_rot = torch.empty((S, N, H, D), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q_rot)
+    lse = torch.empty((S, H, N), dtype=torch.float32, device="cuda")
+    for f in range(2):
+        cache.project_append(0, f, 1, x, w, q_rot)
+        cache.evict(0)
+    assert all(cache.state(0, s)["status"] == 0 for s in range(S))
+    cache.project_append(0, 2, 1, x, w, q_rot)
+    cache.evict(0)                                        # a 3rd keyframe does not fit
+    for s in range(S):
+        st = cache.state(0, s)
+        assert st["status"] == rp.RPKV_ENOSPACE and st["n_special_tokens"] == 12, s
+    cache.project_append(0, 3, 1, x, w, q_rot)
+    for s in range(S):
+        st = cache.state(0, s)
+        assert st["status"] == rp.RPKV_ENOSPACE and st["n_visible_pages"] == 0, s
+    cache.attend(0, q_rot, out, lse)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    cache.reset(0)
+    cache.project_append(0, 0, 1, x, w, q_rot)
+    for s in range(S):
+        st = cache.state(0, s)
+        assert st["status"] == 0 and st["target_page"] == 0 and st["visible_pages"] == [0], s
