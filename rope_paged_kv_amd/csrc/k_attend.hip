@@ -40,8 +40,9 @@ __device__ inline void tile_ref(const AttnArgs& a, int s, int h, int t, int n_pa
 }
 
 // Merge of the key-range splits: out = sum_i w_i O_i / sum_i w_i with
-// w_i = exp(lse_i - max lse); lse = max + log(sum w).  One thread per
-// (stream, head, query, 4 channels).
+// w_i = exp(lse_i - max lse); lse = max + log(sum w).  The partial outputs
+// O_i arrive in fp16, their LSE in fp32.  One thread per (stream, head,
+// query, 4 channels).
 template <typename T>
 __global__ __launch_bounds__(256) void k_attend_combine(AttnArgs a) {
     const size_t idx = blockIdx.x * (size_t)256 + threadIdx.x;
@@ -61,11 +62,11 @@ __global__ __launch_bounds__(256) void k_attend_combine(AttnArgs a) {
         for (int i = 0; i < a.splits; ++i) {
             const size_t row = base + (size_t)i * a.N;
             const float w = __expf(a.part_lse[row] - mx);
-            const float4 o = *(const float4*)(a.part_o + row * kHeadDim + d4 * 4);
-            acc[0] += w * o.x;
-            acc[1] += w * o.y;
-            acc[2] += w * o.z;
-            acc[3] += w * o.w;
+            const uint2 u = *(const uint2*)(a.part_o + row * kHeadDim + d4 * 4);   // 4 fp16
+            acc[0] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(u.x & 0xFFFFu));
+            acc[1] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(u.x >> 16));
+            acc[2] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(u.y & 0xFFFFu));
+            acc[3] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(u.y >> 16));
             wsum += w;
         }
     }

@@ -437,15 +437,25 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
         if (a.lse && hh == 0) a.lse[((size_t)s * a.H + h) * a.N + q] = lse_v;
     } else {
         const size_t row = (((size_t)s * a.H + h) * a.splits + split) * a.N + q;
-        float* op = a.part_o + row * kHeadDim;
+        // Partial outputs in fp16 (RNE): |O_i| is at most max |V|, and 11
+        // significant bits keep the merge well inside the bf16 output's own
+        // rounding while halving the partials' round trip through HBM.
+        uint16_t* op = a.part_o + row * kHeadDim;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d0 = db * 32 + 8 * g + 4 * hh;
                 const f32x16& o = db ? A.o1 : A.o0;
-                *(float4*)(op + d0) = make_float4(o[4 * g] * inv, o[4 * g + 1] * inv,
-                                                  o[4 * g + 2] * inv, o[4 * g + 3] * inv);
+                uint32_t wv[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const _Float16 lo = (_Float16)(o[4 * g + 2 * e] * inv);
+                    const _Float16 hi = (_Float16)(o[4 * g + 2 * e + 1] * inv);
+                    wv[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+                }
+                *(uint2*)(op + d0) = make_uint2(wv[0], wv[1]);
             }
         if (hh == 0) a.part_lse[row] = lse_v;
     }

@@ -121,7 +121,7 @@ bool layout(const kv_config* c, Layout* L) {
     l.off_vsp = l.off_ksp + round_up(caches * l.ksp_elems * l.elem, 256);
     l.off_part_o = l.off_vsp + round_up(caches * l.ksp_elems * l.elem, 256);
     const size_t parts = l.splits > 1 ? (size_t)l.S * l.H * l.splits * l.N : 0;
-    l.off_part_lse = l.off_part_o + round_up(parts * kHeadDim * 4, 256);
+    l.off_part_lse = l.off_part_o + round_up(parts * kHeadDim * 2, 256);   // fp16
     l.total = l.off_part_lse + round_up(parts * 4, 256);
     return true;
 }
@@ -329,7 +329,7 @@ int attend_frame(kv_handle* h, int layer, const void* q_rot, void* out, float* l
     a.vsp = h->base + L.off_vsp + caches_before * L.ksp_elems * L.elem;
     a.kpool_elems = L.kpool_elems;
     a.ksp_elems = L.ksp_elems;
-    a.part_o = (float*)(h->base + L.off_part_o);
+    a.part_o = (uint16_t*)(h->base + L.off_part_o);
     a.part_lse = (float*)(h->base + L.off_part_lse);
     a.S = L.S;
     a.N = L.N;

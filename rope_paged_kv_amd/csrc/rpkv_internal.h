@@ -105,7 +105,7 @@ struct AttnArgs {
     const char* ksp;
     const char* vsp;
     size_t kpool_elems, ksp_elems;
-    float* part_o;          // [S][H][splits][N][D]
+    uint16_t* part_o;       // [S][H][splits][N][D], fp16 bits
     float* part_lse;        // [S][H][splits][N]
     int S, N, H, P, pool, slot_cap, sp_cap, tpp, splits, q_tiles;
     int n_logical;          // workgroups doing work (grid may be padded)
