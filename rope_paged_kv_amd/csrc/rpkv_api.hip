@@ -40,8 +40,9 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 // compute unit (256 on MI355X) issues, so a launch lasts about as long as
 // the most loaded unit needs for its ceil(workgroups / 256) workgroups, and
 // with fewer than 2 workgroups per unit it runs ~1.5x slower per workgroup;
-// splitting shortens each workgroup but adds a round trip of fp32 partial
-// outputs through the merge.  The estimate (microseconds, from measured
+// splitting shortens each workgroup but adds a round trip of partial
+// outputs through the merge (per query, head and split: 64 fp16 channels
+// written and read back, plus the fp32 LSE: 264 bytes).  The estimate (microseconds, from measured
 // rates: ~0.55 us per 64-key tile of a workgroup on a busy unit, ~2 tiles of
 // fixed cost per workgroup, partials moved at ~4 TB/s, ~3 us per merge
 // launch) is taken at the largest visible set the cache can hold.
@@ -49,7 +50,7 @@ int auto_splits(const Layout& L) {
     constexpr int kCUs = 256;
     const long long base = (long long)L.q_tiles * L.H * L.S;
     const int max_tiles = L.pool * L.tpp + (L.sp_cap + kTile - 1) / kTile;
-    const double part_us = (double)L.S * L.H * L.N * 520.0 / 4.0e6;
+    const double part_us = (double)L.S * L.H * L.N * 264.0 / 4.0e6;
     int best = 1;
     double best_us = 0.0;
     for (int s = 1; s <= 32 && s <= max_tiles; ++s) {
