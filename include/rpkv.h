@@ -316,7 +316,7 @@ typedef struct {
     /* byte offsets inside d_mem of the K pool, V pool, K special stream and
      * V special stream (all layers and streams, layout above): inspection only */
     size_t off_kpool, off_vpool, off_ksp, off_vsp;
-    long long frames_appended;  /* kv_append_frame calls (per layer 0) */
+    long long frames_appended;  /* appends of layer 0 (kv_append_frame, kv_append_frame_grid, kv_project_append_frame) */
     long long frames_committed; /* of which commit = 1 */
 } kv_info;
 
