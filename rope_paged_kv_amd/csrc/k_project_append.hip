@@ -226,6 +226,13 @@ __global__ __launch_bounds__(256, 2) void k_project_append(ProjArgs p) {
         uint16_t* kpage = (uint16_t*)a.kpool + s * a.kpool_elems +
                           ((size_t)head * a.pool + tg.page) * a.slot_cap * kHeadDim;
         uint16_t* kspb = (uint16_t*)a.ksp + s * a.ksp_elems + ((size_t)head * a.sp_cap + tg.sp_off) * kHeadDim;
+        // q_rot is read by the attention right after; K rows stream to the page.
+        auto put = [&](uint16_t* dst, const uint4& v) {
+            if (part == 0)
+                *(uint4*)dst = v;
+            else
+                store_stream(dst, v);
+        };
         // Destination of row `row` of this wave (null: nothing to write).
         auto dst_row = [&](int row) -> uint16_t* {
             const int V = V0 + row;
@@ -250,7 +257,7 @@ __global__ __launch_bounds__(256, 2) void k_project_append(ProjArgs p) {
                     f[2 * e] = x * w.x - y * w.y;
                     f[2 * e + 1] = x * w.y + y * w.x;
                 }
-                *(uint4*)(d + c * 8) = Vec<uint16_t>::pack(f);
+                put(d + c * 8, Vec<uint16_t>::pack(f));
             }
         } else {
             const int c0 = pair_chunk<8>(a, lane & 3, 0), c1 = pair_chunk<8>(a, lane & 3, 1);
@@ -269,8 +276,8 @@ __global__ __launch_bounds__(256, 2) void k_project_append(ProjArgs p) {
                     f0[e] = x * w.x - y * w.y;
                     f1[e] = y * w.x + x * w.y;
                 }
-                *(uint4*)(d + c0 * 8) = Vec<uint16_t>::pack(f0);
-                *(uint4*)(d + c1 * 8) = Vec<uint16_t>::pack(f1);
+                put(d + c0 * 8, Vec<uint16_t>::pack(f0));
+                put(d + c1 * 8, Vec<uint16_t>::pack(f1));
             }
         }
     } else if (V0 < a.fP && tg.ok) {
@@ -280,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void k_project_append(ProjArgs p) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int id = lane + 64 * i, d = id >> 3, g = id & 7;
-            *(uint4*)(vpage + (size_t)d * a.slot_cap + g * 8) = *(const uint4*)(stg + d * kPitch + g * 8);
+            store_stream(vpage + (size_t)d * a.slot_cap + g * 8, *(const uint4*)(stg + d * kPitch + g * 8));
         }
     }
 

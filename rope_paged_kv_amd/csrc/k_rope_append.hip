@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
         const bool valid = r < nrows;
         if (valid) {
             *(uint4*)(qrb + r * rs + c * CH) = Vec<T>::pack(fq[i]);
-            if (ok) *(uint4*)(kdst + r * kHeadDim + c * CH) = Vec<T>::pack(fk[i]);
+            if (ok) store_stream(kdst + r * kHeadDim + c * CH, Vec<T>::pack(fk[i]));
         }
         // Rows past the tile's tokens are zeros (padding slots stay zero).
         const uint4 v = valid ? vv[i] : make_uint4(0, 0, 0, 0);
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
             for (int i = 0; i < PER; ++i) {
                 const int id = tid + i * 256;
                 const int d = id / CPR, g = id % CPR;
-                *(uint4*)(vdst + (size_t)d * a.slot_cap + g * CH) = *(const uint4*)&vt[d][g * CH];
+                store_stream(vdst + (size_t)d * a.slot_cap + g * CH, *(const uint4*)&vt[d][g * CH]);
             }
         } else {
             T* vdst = (T*)a.vsp + s * a.ksp_elems + (size_t)h * kHeadDim * a.sp_cap;

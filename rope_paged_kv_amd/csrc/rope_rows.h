@@ -54,6 +54,14 @@ struct Vec<float> {
     }
 };
 
+// 16-byte store that streams past the caches: the pages are read only by
+// later frames' attention, not by anything in this launch or the next one.
+__device__ inline void store_stream(void* dst, const uint4& v) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, (u32x4*)dst);
+}
+
 // Rotation coefficients (cos, sin) of pair j of a token at grid position
 // (hp, wp): the t table for j < pt, the h table for the next ph pairs and the
 // w table after that.
