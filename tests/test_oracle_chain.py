@@ -64,3 +64,24 @@ def test_bf16_chain_close_to_f32_chain():
         _, xa = a.frame(f)
         _, xb = b.frame(f)
         assert np.abs(xa - xb).max() < 2e-2
+
+
+def test_project_qkv_on_one_hot_rows_returns_the_weight_rows():
+    """Token i = e_i picks row i of W: Q, K, V of token i are the three thirds
+    of that row, head h at columns h*D .. h*D+D-1 of each third, rounded once
+    to bf16 (the weights are bf16 already, so exactly the row)."""
+    from oracle.chain import project_qkv
+    rng = np.random.default_rng(7)
+    H, D, C = 2, 4, 8
+    w = rope3d.round_bf16(rng.standard_normal((C, 3 * H * D)))
+    q, k, v = project_qkv(np.eye(C), w, H, D)
+    for i in range(C):
+        for t, got in enumerate((q, k, v)):
+            for h in range(H):
+                np.testing.assert_array_equal(got[i, h], w[i, t * H * D + h * D:t * H * D + (h + 1) * D])
+    # two one-hot tokens: their sum (exact in float64) rounded once to bf16
+    q2, k2, v2 = project_qkv(np.eye(C)[0] + np.eye(C)[[1]], w, H, D)
+    for t, got in enumerate((q2, k2, v2)):
+        want = rope3d.round_bf16(w[0, t * H * D:(t + 1) * H * D] + w[1, t * H * D:(t + 1) * H * D])
+        np.testing.assert_array_equal(got[0].reshape(H * D), want)
+        assert np.any(want != w[0, t * H * D:(t + 1) * H * D] + w[1, t * H * D:(t + 1) * H * D])

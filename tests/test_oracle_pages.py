@@ -186,3 +186,22 @@ def test_keyframe_storage_reduction():
     wl = WORKLOADS[2]
     assert wl.n_keyframes() == 205
     assert 1 - wl.n_keyframes() / wl.frames == pytest.approx(0.8, abs=0.001)
+
+
+@pytest.mark.parametrize("start", [0, 6, 7])
+def test_window_start_matches_a_fresh_simulator(start):
+    """Windowed inference restarts on a fresh cache: the oracle stream's
+    visible frames from `window_start` on equal those of a page simulator
+    that is created at the window's first frame and fed only the window's
+    frames (keyframe schedule and frame indices unchanged)."""
+    from oracle.stream import OracleStream
+    wl = small_variants()["small_skip"]          # keyframe every 3rd frame
+    orc = OracleStream(wl, lambda f, t: None, window_start=start)
+    sim = pages.PageSim(wl.scale_frames, wl.sliding_window, wl.special_page_size, wl.n_special)
+    for f in range(start, wl.frames):
+        assert sim.append(f, wl.is_keyframe(f)) == pages.OK
+        pf, sf = orc.visible(f)
+        assert list(pf) == sim.visible_patch_frames(f), (start, f)
+        assert list(sf) == sim.special_frames + [f], (start, f)   # stored specials, then the frame's own
+        assert all(g >= start for g in pf) and all(g >= start for g in sf), (start, f)
+        sim.evict()
