@@ -245,8 +245,10 @@ def test_attention_small_all_rows(name):
     print(f"{name}: max|out-oracle| {worst:.3e}  max|lse-oracle| {wl_:.3e}")
 
 
-@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("splits", [1, 3, 64])
 def test_attention_split_counts_agree(splits):
+    """64 splits (the largest) over 3 to 9 key tiles: most splits get no tile,
+    end empty (lse -inf) and must weigh nothing in the merge."""
     wl = small_variants()["small_skip"]
     run_and_compare(wl, {0, 5, 9, 19}, splits=splits)
 
