@@ -7,6 +7,22 @@ The functions below carry the C names and only marshal arguments: every step
 runs in the HIP kernels of ``csrc/``.  PyTorch is used for device memory and
 streams (``PagedKVCache`` allocates with torch and passes raw pointers).
 Importing this package loads the library and raises if it is missing.
+
+One layer over a stream of 37x37 frames (6 special tokens + 1369 patches,
+16 heads of 64, bf16)::
+
+    spec = make_spec(max_frames=1024, max_h=37, max_w=37)
+    cfg = make_config(num_layers=1, num_streams=1, num_heads=16, grid_h=37, grid_w=37,
+                      scale_frames=8, sliding_window=16, max_keyframes=256, rope=spec)
+    cache = PagedKVCache(cfg)
+    for f, (q, k, v) in enumerate(frames):        # each [1, 1375, 16, 64] bf16 on the GPU
+        cache.append(0, f, is_keyframe(f), q, k, v, q_rot)   # RoPE + page write
+        cache.attend(0, q_rot, out, lse)                      # paged attention
+        cache.evict(0)                                        # deferred commit / eviction
+
+``cache.project_append`` replaces ``append`` when the frame's hidden states
+and the layer's QKV weight are at hand (the projection runs in the same
+kernel).
 """
 from __future__ import annotations
 
