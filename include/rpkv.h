@@ -247,6 +247,18 @@ int kv_project_append_frame(kv_handle* h, int layer, int frame_idx, int commit, 
                             void* stream);
 
 /*
+ * kv_project_append_frame for a frame of its own patch grid, exactly as
+ * kv_append_frame_grid is kv_append_frame for one ([ROPE-KV] FAQ on variable
+ * numbers of patches per frame): x keeps its [S][N][hidden] shape, only the
+ * frame's first special_tokens + grid_h*grid_w rows are read, and only those
+ * rows of q_rot are written; the page records its token count.  EINVAL on a
+ * grid outside the bounds kv_append_frame_grid accepts, and as above.
+ */
+int kv_project_append_frame_grid(kv_handle* h, int layer, int frame_idx, int commit, int grid_h,
+                                 int grid_w, const void* x, int hidden, const void* w, void* q_rot,
+                                 const void* d_tables, void* stream);
+
+/*
  * Attention of the frame's N query tokens (all heads, all streams) over the
  * visible page table of `layer` ([ROPE-KV] "Attention Computation with Cached
  * RoPE"; [RT3D] "Per-Frame Processing and Causal Attention"):

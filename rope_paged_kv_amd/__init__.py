@@ -102,6 +102,14 @@ def kv_project_append_frame(h, layer: int, frame_idx: int, commit: int, x, hidde
            "kv_project_append_frame")
 
 
+def kv_project_append_frame_grid(h, layer: int, frame_idx: int, commit: int, grid_h: int,
+                                 grid_w: int, x, hidden: int, w, q_rot, d_tables, stream: int) -> None:
+    _check(_lib.kv_project_append_frame_grid(h, layer, frame_idx, int(commit), grid_h, grid_w,
+                                             _vp(x), hidden, _vp(w), _vp(q_rot), _vp(d_tables),
+                                             stream),
+           "kv_project_append_frame_grid")
+
+
 def attend_frame(h, layer: int, q_rot, out, lse, stream: int) -> None:
     _check(_lib.attend_frame(h, layer, _vp(q_rot), _vp(out), _vp(lse), stream), "attend_frame")
 
@@ -228,16 +236,21 @@ class PagedKVCache:
             kv_append_frame_grid(self.h, layer, frame_idx, commit, grid[0], grid[1], q, k, v,
                                  q_rot, self.tables, self.stream)
 
-    def project_append(self, layer, frame_idx, commit, x, w, q_rot):
-        """Fused projection + RoPE + append: x [S][N][hidden] bf16, w [3*H*D][hidden] bf16."""
+    def project_append(self, layer, frame_idx, commit, x, w, q_rot, grid=None):
+        """Fused projection + RoPE + append: x [S][N][hidden] bf16, w [3*H*D][hidden] bf16;
+        grid: this frame's (grid_h, grid_w) if it differs from the configured one."""
         c, bf = self.cfg, self.torch.bfloat16
         n = c.special_tokens + c.grid_h * c.grid_w
         hidden = x.shape[-1]
         self._expect("x", x, (c.num_streams, n, hidden), bf)
         self._expect("w", w, (3 * c.num_heads * c.head_dim, hidden), bf)
         self._act("q_rot", q_rot)
-        kv_project_append_frame(self.h, layer, frame_idx, commit, x, x.shape[-1], w, q_rot,
-                                self.tables, self.stream)
+        if grid is None:
+            kv_project_append_frame(self.h, layer, frame_idx, commit, x, hidden, w, q_rot,
+                                    self.tables, self.stream)
+        else:
+            kv_project_append_frame_grid(self.h, layer, frame_idx, commit, grid[0], grid[1], x,
+                                         hidden, w, q_rot, self.tables, self.stream)
 
     def attend(self, layer, q_rot, out, lse=None):
         self._act("q_rot", q_rot)

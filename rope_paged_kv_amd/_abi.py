@@ -11,7 +11,7 @@ RPKV_MAX_POOL_PAGES = 512
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librpkv.so")
 
 EXPORTS = ("rope3d_tables_bytes", "rope3d_build_tables", "kv_required_bytes", "kv_create",
-           "kv_destroy", "kv_reset", "kv_append_frame", "kv_append_frame_grid", "kv_project_append_frame", "attend_frame",
+           "kv_destroy", "kv_reset", "kv_append_frame", "kv_append_frame_grid", "kv_project_append_frame", "kv_project_append_frame_grid", "attend_frame",
            "kv_evict_deferred",
            "kv_rollback", "kv_read_state", "kv_get_info", "rpkv_strerror")
 
@@ -79,6 +79,7 @@ def load() -> C.CDLL:
         "kv_append_frame": (i, [vp, i, i, i, vp, vp, vp, vp, vp, vp]),
         "kv_append_frame_grid": (i, [vp, i, i, i, i, i, vp, vp, vp, vp, vp, vp]),
         "kv_project_append_frame": (i, [vp, i, i, i, vp, i, vp, vp, vp, vp]),
+        "kv_project_append_frame_grid": (i, [vp, i, i, i, i, i, vp, i, vp, vp, vp, vp]),
         "attend_frame": (i, [vp, i, vp, vp, vp, vp]),
         "kv_evict_deferred": (i, [vp, i, vp]),
         "kv_rollback": (i, [vp, i, vp]),

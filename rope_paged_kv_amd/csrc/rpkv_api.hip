@@ -291,7 +291,18 @@ int kv_append_frame_grid(kv_handle* h, int layer, int frame_idx, int commit, int
 int kv_project_append_frame(kv_handle* h, int layer, int frame_idx, int commit, const void* x,
                             int hidden, const void* w, void* q_rot, const void* d_tables,
                             void* stream) {
+    if (!h) return RPKV_EINVAL;
+    return kv_project_append_frame_grid(h, layer, frame_idx, commit, h->cfg.grid_h, h->cfg.grid_w, x,
+                                        hidden, w, q_rot, d_tables, stream);
+}
+
+int kv_project_append_frame_grid(kv_handle* h, int layer, int frame_idx, int commit, int grid_h,
+                                 int grid_w, const void* x, int hidden, const void* w, void* q_rot,
+                                 const void* d_tables, void* stream) {
     if (!h || layer < 0 || layer >= h->cfg.num_layers) return RPKV_EINVAL;
+    if (grid_h < 1 || grid_w < 1 || grid_h > h->cfg.rope.max_h || grid_w > h->cfg.rope.max_w ||
+        (long long)grid_h * grid_w > h->L.P)
+        return RPKV_EINVAL;
     if (h->cfg.dtype != RPKV_BF16 || h->L.H % 2 != 0) return RPKV_EINVAL;
     if (frame_idx < 0 || frame_idx >= h->cfg.rope.max_frames || (commit != 0 && commit != 1))
         return RPKV_EINVAL;
@@ -299,8 +310,8 @@ int kv_project_append_frame(kv_handle* h, int layer, int frame_idx, int commit, 
     if (!x || !w || !q_rot || !d_tables) return RPKV_EINVAL;
     if (!aligned16(x) || !aligned16(w) || !aligned16(q_rot) || !aligned16(d_tables)) return RPKV_EINVAL;
     ProjArgs p;
-    p.a = append_args(h, layer, frame_idx, commit, h->cfg.grid_h, h->cfg.grid_w, nullptr, nullptr,
-                      nullptr, q_rot, d_tables);
+    p.a = append_args(h, layer, frame_idx, commit, grid_h, grid_w, nullptr, nullptr, nullptr, q_rot,
+                      d_tables);
     p.x = (const uint16_t*)x;
     p.w = (const uint16_t*)w;
     p.C = hidden;

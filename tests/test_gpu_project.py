@@ -107,6 +107,9 @@ def test_project_append_checks_its_arguments():
     f32 = make_cache(small_variants()["small_f32"])
     with pytest.raises(rp.RpkvError):
         rp.kv_project_append_frame(f32.h, 0, 0, 1, x, C, w, q_rot, f32.tables, f32.stream)
+    for grid in ((14, 17), (13, 18), (0, 5), (17, 13)):    # configured grid 13x17
+        with pytest.raises(rp.RpkvError):
+            cache.project_append(0, 0, 1, x, w, q_rot, grid=grid)
 
 
 def test_project_append_shares_the_overflow_rule():
@@ -143,3 +146,58 @@ def test_project_append_shares_the_overflow_rule():
     for s in range(S):
         st = cache.state(0, s)
         assert st["status"] == 0 and st["target_page"] == 0 and st["visible_pages"] == [0], s
+
+
+def test_project_append_variable_grids():
+    """Frames of their own grids through the fused path (13x17, 11x17, 5x6,
+    1x1, 13x9 in 13x17 pages): page token counts, q_rot of the frame's rows,
+    K pages of the frame's patches and attention of its tokens against the
+    oracle; rows past the frame keep what they held."""
+    wl = small_variants()["small_proj"].replace(grids=((13, 17), (11, 17), (5, 6), (1, 1), (13, 9)),
+                                                frames=7)
+    S, H, D, ns = wl.streams, wl.heads, wl.head_dim, wl.n_special
+    cache = make_cache(wl)
+    sim = pages.PageSim(wl.scale_frames, wl.sliding_window, wl.special_page_size, wl.n_special)
+    w = projection(wl, 0, n_out=3 * H * D)
+    w_dev = to_dev(w.T, torch.bfloat16)
+    proj = {}
+
+    def source(s):
+        def get(f, t):
+            if (s, f) not in proj:
+                proj[(s, f)] = project_qkv(embeddings(wl, s, f), w, H, D)
+            return proj[(s, f)][t]
+        return get
+
+    orc = {s: OracleStream(wl, source(s)) for s in range(S)}
+    shape = (S, wl.tokens, H, D)
+    q_rot = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((S, H, wl.tokens), dtype=torch.float32, device="cuda")
+    for f in range(wl.frames):
+        gh, gw = wl.grid_of(f)
+        n, commit = ns + gh * gw, wl.is_keyframe(f)
+        x = np.stack([embeddings(wl, s, f) for s in range(S)])
+        q_rot.fill_(7.0)
+        out.fill_(7.0)
+        cache.project_append(0, f, int(commit), to_dev(x, torch.bfloat16), w_dev, q_rot, grid=(gh, gw))
+        sim.append(f, commit)
+        cache.attend(0, q_rot, out, lse)
+        torch.cuda.synchronize()
+        want_pt = {p: wl.grid_of(g)[0] * wl.grid_of(g)[1] for p, g in sim.page_frame.items()}
+        want_pt[sim.target] = gh * gw
+        for s in range(S):
+            st = cache.state(0, s)
+            assert st["query_tokens"] == n and st["visible_pages"] == sim.visible.patch_pages, (f, s)
+            for p, cnt in want_pt.items():
+                assert st["page_tokens"][p] == cnt, (f, s, p)
+            assert np.abs(q_rot[s, :n].float().cpu().numpy() - orc[s].q_rot(f)).max() <= BF16_TOL, (f, s)
+            assert torch.all(q_rot[s, n:] == 7.0) and torch.all(out[s, n:] == 7.0), (f, s)
+            kp = _views(cache, s)[0]
+            got_k = kp[:, sim.target, :gh * gw].float().cpu().numpy().transpose(1, 0, 2)
+            assert np.abs(got_k - orc[s].kv(f)[0][ns:]).max() <= BF16_TOL, (f, s)
+            o_want, lse_want = orc[s].attend(f)
+            assert np.abs(out[s, :n].float().cpu().numpy() - o_want).max() <= BF16_TOL, (f, s)
+            assert np.abs(lse[s, :, :n].cpu().numpy() - lse_want).max() <= LSE_TOL, (f, s)
+        sim.evict()
+        cache.evict(0)
