@@ -256,19 +256,19 @@ def bench_full_depth(wl, args, dev):
     F = wl.frames
     x = torch.empty_like(x0[0])
 
-    def one_pass(ev=None):
+    def one_pass(ev=None, pev=None):
         fds.reset()
         for f in range(F):
             x.copy_(x0[f])
-            fds.frame(f, x, events=ev)
+            fds.frame(f, x, events=ev, proj_events=pev)
 
     for _ in range(args.warmup):
         one_pass()
     torch.cuda.synchronize()
-    evs = []
+    evs, pevs = [], []
     t0 = time.perf_counter()
     for k in range(args.steps):
-        one_pass(evs)
+        one_pass(evs, pevs)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     att_ms, flops = [], []
@@ -283,6 +283,11 @@ def bench_full_depth(wl, args, dev):
     extra = {"attend_tflops_global_layers": round(float(flops[glob].mean() / (att_ms[glob].mean() / 1e3) / 1e12), 2),
              "attend_tflops_frame_layers": round(float(flops[~glob].mean() / (att_ms[~glob].mean() / 1e3) / 1e12), 2),
              "frame_steps_per_s": round(F * args.steps / elapsed, 3)}
+    proj_us = float(np.mean([e0.elapsed_time(e1) for (_, _, e0, e1) in pevs])) * 1e3
+    proj_flops = 2.0 * wl.streams * wl.tokens * wl.hidden * 3 * wl.heads * wl.head_dim
+    extra.update({"project_append_avg_us": round(proj_us, 2),
+                  "project_append_tflops": round(proj_flops / proj_us / 1e6, 1),
+                  "project_append_mfma_frac": round(proj_flops / proj_us / 1e6 / BF16_PEAK_TFLOPS, 4)})
     res = result_line(wl, args, elapsed, F * wl.streams, att_ms, flops, None,
                       fds.global_cache.info()["attn_splits"], unit="stream-frames/s", extra=extra,
                       config_extra={"layers": wl.chain_layers, "hidden": wl.hidden,

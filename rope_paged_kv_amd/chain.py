@@ -62,16 +62,23 @@ class FullDepthStream:
         self.frame_cache.reset(-1)
 
     def frame(self, f: int, x: torch.Tensor, keep: Optional[List[torch.Tensor]] = None,
-              events: Optional[list] = None) -> torch.Tensor:
+              events: Optional[list] = None, proj_events: Optional[list] = None) -> torch.Tensor:
         """Runs frame f (x: fp32 [S][N][hidden], updated in place) through all
         layers; appends each layer's attention output to `keep` if given, and
         (frame, layer, start event, end event) around each attention launch to
-        `events` if given."""
+        `events` (around each fused projection + append to `proj_events`) if
+        given."""
         commit = int(f % self.interval == 0)
         for layer in range(self.L):
             self.xb.copy_(x)
             c, g, cm = (self.frame_cache, 0, 0) if layer % 2 == 0 else (self.global_cache, layer // 2, commit)
+            if proj_events is not None:
+                p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                p0.record()
             c.project_append(g, f, cm, self.xb, self.w[layer], self.q_rot)
+            if proj_events is not None:
+                p1.record()
+                proj_events.append((f, layer, p0, p1))
             if events is not None:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
