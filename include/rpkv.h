@@ -144,7 +144,11 @@ int rope3d_build_tables(const rope3d_spec* spec, void* d_tables, size_t bytes, v
  *    [layer][stream][head][D][token] (same 16-slot order), token capacity
  *    rounded up to 64;
  *  - attention split scratch (partial outputs).
- * Slots beyond a page's tokens stay zero.
+ * Padding: kv_create zero-fills everything.  An append zeroes the V^T padding
+ * of the 64-slot tiles it writes; the K padding, and V^T tiles past the
+ * frame's last tile, keep what they held, so a page recycled for a frame of a
+ * smaller grid may hold an older frame's rows there.  Attention masks every
+ * slot past a page's token count, so such rows never reach the softmax.
  */
 typedef struct {
     int num_layers;         /* caches per stream (one per attention layer) */
@@ -314,7 +318,8 @@ typedef struct {
 int kv_read_state(kv_handle* h, int layer, int stream_idx, kv_state_host* out, void* stream);
 
 /* Static sizes of a handle plus host-side counters of the calls made
- * ([KVB] "Working with the KV Cache API": get_kv_cache_info). */
+ * ([KVB] "Working with the KV Cache API": get_kv_cache_info).  Reads nothing
+ * from the device. */
 typedef struct {
     int num_layers, num_streams, num_heads, head_dim, dtype;
     int tokens_per_frame;       /* N */
@@ -328,8 +333,13 @@ typedef struct {
     /* byte offsets inside d_mem of the K pool, V pool, K special stream and
      * V special stream (all layers and streams, layout above): inspection only */
     size_t off_kpool, off_vpool, off_ksp, off_vsp;
-    long long frames_appended;  /* appends of layer 0 (kv_append_frame, kv_append_frame_grid, kv_project_append_frame) */
-    long long frames_committed; /* of which commit = 1 */
+    long long frames_appended;  /* appends of layer 0 (every append entry point) since
+                                   kv_create or the last kv_reset of layer 0 / all layers */
+    long long frames_committed; /* layer-0 appends with commit = 1 that kv_evict_deferred
+                                   then kept: not dropped by kv_rollback, not replaced by
+                                   a second append.  Host-side count: a commit the device
+                                   refuses (special stream full: sticky RPKV_ENOSPACE,
+                                   seen with kv_read_state) is still counted */
 } kv_info;
 
 int kv_get_info(const kv_handle* h, kv_info* out);

@@ -40,9 +40,10 @@ __device__ inline void tile_ref(const AttnArgs& a, int s, int h, int t, int n_pa
 }
 
 // Merge of the key-range splits: out = sum_i w_i O_i / sum_i w_i with
-// w_i = exp(lse_i - max lse); lse = max + log(sum w).  The partial outputs
-// O_i arrive in fp16, their LSE in fp32.  One thread per (stream, head,
-// query, 4 channels).
+// w_i = exp(lse_i - max lse); lse = max + log(sum w).  Split i's partial
+// output arrives as fp16 words scaled by a power of two and the fp32 factor
+// f_i that undoes it (O_i = f_i * words), beside its LSE.  One thread per
+// (stream, head, query, 4 channels).
 template <typename T>
 __global__ __launch_bounds__(256) void k_attend_combine(AttnArgs a) {
     const size_t idx = blockIdx.x * (size_t)256 + threadIdx.x;
@@ -56,17 +57,19 @@ __global__ __launch_bounds__(256) void k_attend_combine(AttnArgs a) {
     if (q >= a.states[s].n_query) return;   // not a token of this frame
     const size_t base = (size_t)sh * a.splits * a.N + q;
     float mx = -INFINITY;
-    for (int i = 0; i < a.splits; ++i) mx = fmaxf(mx, a.part_lse[base + (size_t)i * a.N]);
+    for (int i = 0; i < a.splits; ++i) mx = fmaxf(mx, a.part_ls[base + (size_t)i * a.N].x);
     float acc[4] = {0.f, 0.f, 0.f, 0.f}, wsum = 0.f;
     if (mx > -INFINITY) {
         for (int i = 0; i < a.splits; ++i) {
             const size_t row = base + (size_t)i * a.N;
-            const float w = __expf(a.part_lse[row] - mx);
+            const float2 ls = a.part_ls[row];
+            const float w = __expf(ls.x - mx);
+            const float wf = w * ls.y;
             const uint2 u = *(const uint2*)(a.part_o + row * kHeadDim + d4 * 4);   // 4 fp16
-            acc[0] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(u.x & 0xFFFFu));
-            acc[1] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(u.x >> 16));
-            acc[2] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(u.y & 0xFFFFu));
-            acc[3] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(u.y >> 16));
+            acc[0] += wf * (float)__builtin_bit_cast(_Float16, (uint16_t)(u.x & 0xFFFFu));
+            acc[1] += wf * (float)__builtin_bit_cast(_Float16, (uint16_t)(u.x >> 16));
+            acc[2] += wf * (float)__builtin_bit_cast(_Float16, (uint16_t)(u.y & 0xFFFFu));
+            acc[3] += wf * (float)__builtin_bit_cast(_Float16, (uint16_t)(u.y >> 16));
             wsum += w;
         }
     }

@@ -415,6 +415,12 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
     const bool empty = !(l > 0.f);
     const float inv = empty ? 0.f : 1.f / l;
     const float lse_v = empty ? -INFINITY : (A.M + __log2f(l)) * 0.69314718055994531f;
+    // Largest accumulator of the query (both half-waves hold 32 of its 64
+    // channels): the split path scales its row by it.
+    float mo = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mo = max3f(mo, fabsf(A.o0[r]), fabsf(A.o1[r]));
+    mo = fmaxf(mo, __shfl_xor(mo, 32));
     if (!qvalid) return;
     if (a.splits == 1) {
         uint16_t* op = (uint16_t*)a.out + (((size_t)s * a.N + q) * a.H + h) * kHeadDim;
@@ -437,9 +443,16 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
         if (a.lse && hh == 0) a.lse[((size_t)s * a.H + h) * a.N + q] = lse_v;
     } else {
         const size_t row = (((size_t)s * a.H + h) * a.splits + split) * a.N + q;
-        // Partial outputs in fp16 (RNE): |O_i| is at most max |V|, and 11
-        // significant bits keep the merge well inside the bf16 output's own
-        // rounding while halving the partials' round trip through HBM.
+        // Partial outputs in fp16 (RNE), each row scaled by the power of two
+        // 2^-e that brings its largest accumulator into [1, 2) (e clamped to
+        // [-126, 126]), so fp16 keeps 11 significant bits of every row
+        // whatever the range of V: no overflow for large V, no subnormals for
+        // small V.  The row's factor 2^e / l goes to the merge in fp32 beside
+        // the LSE.  Scaling by a power of two is exact, so V scaled by 2^k
+        // gives exactly the same fp16 words.
+        const int b = min(max((int)(__float_as_uint(mo) >> 23), 1), 253);   // biased exponent
+        const float down = __uint_as_float((uint32_t)(254 - b) << 23);      // 2^-e
+        const float fac = inv * __uint_as_float((uint32_t)b << 23);         // 2^e / l
         uint16_t* op = a.part_o + row * kHeadDim;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
@@ -450,14 +463,14 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
                 uint32_t wv[2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const _Float16 lo = (_Float16)(o[4 * g + 2 * e] * inv);
-                    const _Float16 hi = (_Float16)(o[4 * g + 2 * e + 1] * inv);
+                    const _Float16 lo = (_Float16)(o[4 * g + 2 * e] * down);
+                    const _Float16 hi = (_Float16)(o[4 * g + 2 * e + 1] * down);
                     wv[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
                             ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
                 }
                 *(uint2*)(op + d0) = make_uint2(wv[0], wv[1]);
             }
-        if (hh == 0) a.part_lse[row] = lse_v;
+        if (hh == 0) a.part_ls[row] = make_float2(lse_v, fac);
     }
 }
 

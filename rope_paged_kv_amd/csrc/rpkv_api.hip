@@ -18,6 +18,7 @@ struct kv_handle {
     char* base;
     size_t bytes;
     long long appended, committed;
+    bool pending0;   // layer 0's last append asked to be kept and was neither kept nor dropped yet
 };
 
 namespace {
@@ -42,7 +43,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 // with fewer than 2 workgroups per unit it runs ~1.5x slower per workgroup;
 // splitting shortens each workgroup but adds a round trip of partial
 // outputs through the merge (per query, head and split: 64 fp16 channels
-// written and read back, plus the fp32 LSE: 264 bytes).  The estimate (microseconds, from measured
+// plus the fp32 LSE and row factor, written and read back: 272 bytes).  The
+// estimate (microseconds, from measured
 // rates: ~0.55 us per 64-key tile of a workgroup on a busy unit, ~2 tiles of
 // fixed cost per workgroup, partials moved at ~4 TB/s, ~3 us per merge
 // launch) is taken at the largest visible set the cache can hold.
@@ -50,7 +52,7 @@ int auto_splits(const Layout& L) {
     constexpr int kCUs = 256;
     const long long base = (long long)L.q_tiles * L.H * L.S;
     const int max_tiles = L.pool * L.tpp + (L.sp_cap + kTile - 1) / kTile;
-    const double part_us = (double)L.S * L.H * L.N * 264.0 / 4.0e6;
+    const double part_us = (double)L.S * L.H * L.N * 272.0 / 4.0e6;
     int best = 1;
     double best_us = 0.0;
     for (int s = 1; s <= 32 && s <= max_tiles; ++s) {
@@ -122,8 +124,8 @@ bool layout(const kv_config* c, Layout* L) {
     l.off_vsp = l.off_ksp + round_up(caches * l.ksp_elems * l.elem, 256);
     l.off_part_o = l.off_vsp + round_up(caches * l.ksp_elems * l.elem, 256);
     const size_t parts = l.splits > 1 ? (size_t)l.S * l.H * l.splits * l.N : 0;
-    l.off_part_lse = l.off_part_o + round_up(parts * kHeadDim * 2, 256);   // fp16
-    l.total = l.off_part_lse + round_up(parts * 4, 256);
+    l.off_part_ls = l.off_part_o + round_up(parts * kHeadDim * 2, 256);   // fp16 words
+    l.total = l.off_part_ls + round_up(parts * 8, 256);                   // (LSE, factor)
     return true;
 }
 
@@ -188,6 +190,7 @@ int kv_create(const kv_config* cfg, void* d_mem, size_t bytes, void* stream, kv_
     h->base = (char*)d_mem;
     h->bytes = bytes;
     h->appended = h->committed = 0;
+    h->pending0 = false;
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = launch_fill_zero(d_mem, L.total, st);
     if (e == hipSuccess) e = launch_reset(states_of(h, 0), cfg->num_layers * L.S, st);
@@ -208,7 +211,10 @@ int kv_reset(kv_handle* h, int layer, void* stream) {
     if (!h || layer < -1 || layer >= h->cfg.num_layers) return RPKV_EINVAL;
     const int first = layer < 0 ? 0 : layer;
     const int count = (layer < 0 ? h->cfg.num_layers : 1) * h->L.S;
-    if (layer <= 0) h->appended = h->committed = 0;
+    if (layer <= 0) {
+        h->appended = h->committed = 0;
+        h->pending0 = false;
+    }
     return hip_status(launch_reset(states_of(h, first), count, (hipStream_t)stream));
 }
 
@@ -283,7 +289,7 @@ int kv_append_frame_grid(kv_handle* h, int layer, int frame_idx, int commit, int
     const int rc = hip_status(launch_rope_append(a, h->cfg.dtype, (hipStream_t)stream));
     if (rc == RPKV_OK && layer == 0) {
         h->appended++;
-        h->committed += commit;
+        h->pending0 = commit != 0;   // replaces an append not yet kept or dropped
     }
     return rc;
 }
@@ -320,7 +326,7 @@ int kv_project_append_frame_grid(kv_handle* h, int layer, int frame_idx, int com
     const int rc = hip_status(launch_project_append(p, (hipStream_t)stream));
     if (rc == RPKV_OK && layer == 0) {
         h->appended++;
-        h->committed += commit;
+        h->pending0 = commit != 0;
     }
     return rc;
 }
@@ -342,7 +348,7 @@ int attend_frame(kv_handle* h, int layer, const void* q_rot, void* out, float* l
     a.kpool_elems = L.kpool_elems;
     a.ksp_elems = L.ksp_elems;
     a.part_o = (uint16_t*)(h->base + L.off_part_o);
-    a.part_lse = (float*)(h->base + L.off_part_lse);
+    a.part_ls = (float2*)(h->base + L.off_part_ls);
     a.S = L.S;
     a.N = L.N;
     a.H = L.H;
@@ -362,14 +368,20 @@ int attend_frame(kv_handle* h, int layer, const void* q_rot, void* out, float* l
 int kv_evict_deferred(kv_handle* h, int layer, void* stream) {
     if (!h || layer < 0 || layer >= h->cfg.num_layers) return RPKV_EINVAL;
     const Layout& L = h->L;
-    return hip_status(launch_evict(states_of(h, layer), L.S, L.sf, L.W, L.max_kf * L.nsp, L.nsp,
-                                   (hipStream_t)stream));
+    const int rc = hip_status(launch_evict(states_of(h, layer), L.S, L.sf, L.W, L.max_kf * L.nsp,
+                                           L.nsp, (hipStream_t)stream));
+    if (rc == RPKV_OK && layer == 0 && h->pending0) {
+        h->committed++;
+        h->pending0 = false;
+    }
+    return rc;
 }
 
 int kv_rollback(kv_handle* h, int layer, void* stream) {
     if (!h || layer < 0 || layer >= h->cfg.num_layers) return RPKV_EINVAL;
-    if (layer == 0 && h->committed > 0) h->committed--;
-    return hip_status(launch_rollback(states_of(h, layer), h->L.S, (hipStream_t)stream));
+    const int rc = hip_status(launch_rollback(states_of(h, layer), h->L.S, (hipStream_t)stream));
+    if (rc == RPKV_OK && layer == 0) h->pending0 = false;
+    return rc;
 }
 
 int kv_read_state(kv_handle* h, int layer, int stream_idx, kv_state_host* out, void* stream) {

@@ -59,7 +59,7 @@ struct Layout {
     size_t kpool_elems; // per cache (K; V has the same count)
     size_t ksp_elems;   // per cache
     // byte offsets inside the handle's device memory
-    size_t off_state, off_kpool, off_vpool, off_ksp, off_vsp, off_part_o, off_part_lse, total;
+    size_t off_state, off_kpool, off_vpool, off_ksp, off_vsp, off_part_o, off_part_ls, total;
 };
 
 struct AppendArgs {
@@ -105,8 +105,8 @@ struct AttnArgs {
     const char* ksp;
     const char* vsp;
     size_t kpool_elems, ksp_elems;
-    uint16_t* part_o;       // [S][H][splits][N][D], fp16 bits
-    float* part_lse;        // [S][H][splits][N]
+    uint16_t* part_o;       // [S][H][splits][N][D], fp16 bits, each row scaled by 2^-e
+    float2* part_ls;        // [S][H][splits][N]: (LSE, factor 2^e / l of the row)
     int S, N, H, P, pool, slot_cap, sp_cap, tpp, splits, q_tiles;
     int n_logical;          // workgroups doing work (grid may be padded)
     float scale;            // 1/sqrt(D)

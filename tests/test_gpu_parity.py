@@ -128,6 +128,38 @@ def test_append_without_eviction_and_rollback():
         assert cache.state()["pending_commit"] == int(sim.pending is not None), f
 
 
+def test_info_counts_appended_and_kept_frames():
+    """kv_get_info's host counters across a skip-append, a rollback, an append
+    replaced by a second one, and a reset; the device's committed special
+    tokens agree (6 per kept frame)."""
+    wl = small_variants()["small_bf16"]
+    cache = make_cache(wl)
+    run = Runner(wl, cache)
+    z = torch.zeros((1, wl.tokens, wl.heads, wl.head_dim), dtype=run.dt, device="cuda")
+    script = [  # (frame, commit, action, appended, kept)
+        (0, 1, "evict", 1, 1),
+        (1, 0, "evict", 2, 1),        # skip-append: not kept
+        (2, 1, "rollback", 3, 1),     # dropped
+        (2, 1, "none", 4, 1),         # pending ...
+        (3, 1, "evict", 5, 2),        # ... replaced by this one: one frame kept
+        (4, 0, "rollback", 6, 2),
+        (5, 1, "evict", 7, 3),
+    ]
+    for f, c, act, n_app, n_kept in script:
+        cache.append(0, f, c, z, z, z, run.q_rot)
+        if act == "evict":
+            cache.evict(0)
+        elif act == "rollback":
+            cache.rollback(0)
+            cache.evict(0)                 # a no-op after a rollback
+        info = cache.info()
+        assert (info["frames_appended"], info["frames_committed"]) == (n_app, n_kept), (f, act, info)
+        assert cache.state()["n_special_tokens"] == wl.n_special * n_kept, (f, act)
+    cache.reset(-1)
+    info = cache.info()
+    assert (info["frames_appended"], info["frames_committed"]) == (0, 0)
+
+
 def test_special_stream_overflow_is_sticky_and_reset_recovers():
     wl = small_variants()["small_bf16"]
     cache = make_cache(wl, max_keyframes=3)
@@ -251,6 +283,50 @@ def test_attention_split_counts_agree(splits):
     end empty (lse -inf) and must weigh nothing in the merge."""
     wl = small_variants()["small_skip"]
     run_and_compare(wl, {0, 5, 9, 19}, splits=splits)
+
+
+@pytest.mark.parametrize("log2_scale", [17, -20])
+def test_attention_is_linear_in_v_at_every_split_count(log2_scale):
+    """V scaled by 2^k, k = 17 (|V| up to ~7e5, past fp16's largest value) and
+    k = -20 (|V| ~ 1e-6, below fp16's normal range), at split counts 1, 3 and
+    the automatic one.  Attention is linear in V and a power of two scales
+    every product, partial and rounding exactly, so each output equals 2^k
+    times the unscaled run of the same split count bit for bit, the LSE is
+    unchanged, and the output is within 2^k * 2e-2 of the oracle fed the
+    scaled V (the usual bar, relative to the scale of V)."""
+    wl = small_variants()["small_skip"]
+    k = float(2.0 ** log2_scale)
+
+    def gen(scale):
+        return lambda f, t: qkv(wl, 0, 0, f, t) * (scale if t == 2 else 1.0)
+
+    orc = OracleStream(wl, gen(k))
+    check = {0, 3, 9, 19}
+    for splits in (1, 3, 0):
+        outs = {}
+        for scale in (1.0, k):
+            cache = make_cache(wl, splits=splits)
+            run = Runner(wl, cache)
+            g = gen(scale)
+            got = {}
+            for f in range(wl.frames):
+                q, kk, v = (to_dev(g(f, t)[None], run.dt) for t in range(3))
+                run.frame(f, q, kk, v, wl.is_keyframe(f))
+                if f in check:
+                    got[f] = (run.out.clone(), run.lse.clone())
+            outs[scale] = got
+            if splits == 0:
+                assert cache.info()["attn_splits"] > 1
+        for f in check:
+            o1, l1 = outs[1.0][f]
+            ok, lk = outs[k][f]
+            assert torch.isfinite(ok.float()).all(), (splits, f)
+            assert torch.equal(ok, (o1.float() * k).to(ok.dtype)), (splits, f)
+            assert torch.equal(lk, l1), (splits, f)
+            o, lse = orc.attend(f)
+            err = np.abs(ok[0].float().cpu().numpy() - o).max()
+            assert err <= BF16_TOL * k, (splits, f, err / k)
+            assert np.abs(lk[0].cpu().numpy() - lse).max() <= LSE_TOL, (splits, f)
 
 
 def test_tiny_f32_full():
