@@ -134,6 +134,13 @@ def small_variants() -> dict:
         "small_chain": Workload("small_chain_6x6", "bf16", frames=7, grid_h=6, grid_w=6, heads=4,
                                 streams=2, cached_layers=2, scale_frames=1, sliding_window=2,
                                 keyframe_interval=2, chain_layers=4, hidden=256),
+        # the full-depth stack's structure (4 streams, 24 alternating layers,
+        # keyframe every 2nd frame) at a size the oracle chain runs in
+        # seconds, long enough for the first eviction (frame 10) and the
+        # first recycled page (frame 12)
+        "small_depth": Workload("small_depth_6x6", "bf16", frames=16, grid_h=6, grid_w=6, heads=4,
+                                streams=4, cached_layers=12, scale_frames=2, sliding_window=3,
+                                keyframe_interval=2, chain_layers=24, hidden=256),
         # the 2D module's arrangement: y and x halves, base frequency 100
         "small_rope2d": Workload("small_rope2d_10x7", "bf16", frames=8, grid_h=10, grid_w=7, heads=2,
                                  scale_frames=1, sliding_window=3, keyframe_interval=1,

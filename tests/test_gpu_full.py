@@ -1,7 +1,8 @@
 """GPU parity at the full workload sizes, on sampled outputs the oracle
 computes one by one: the long keyframe-interval stream, the 64x64 grid, the
 four-stream cache geometry of the full-depth stack, and the full-depth chain
-(projection, alternating frame/global layers, residual) on its first frames.
+(projection, alternating frame/global layers, residual): at full size on its
+first frames, and at a reduced size through eviction and page recycling.
 
 Bars as in test_gpu_parity: bf16 outputs within 2e-2 max-abs of the float64
 oracle, LSE within 1e-2, page tables bit-exact."""
@@ -125,45 +126,78 @@ def test_full_depth_cache_geometry_four_streams():
         assert st["n_special_tokens"] == 6 * 128 and st["fresh"] == 41, s
 
 
+def _chain(wl, frames=None):
+    from rope_paged_kv_amd.chain import FullDepthStream
+    weights = [to_dev(projection(wl, l), torch.bfloat16) for l in range(wl.chain_layers)]
+    return FullDepthStream(streams=wl.streams, layers=wl.chain_layers, heads=wl.heads,
+                           grid_h=wl.grid_h, grid_w=wl.grid_w, scale_frames=wl.scale_frames,
+                           sliding_window=wl.sliding_window, keyframe_interval=wl.keyframe_interval,
+                           frames=wl.frames if frames is None else frames, weights=weights)
+
+
+def _chain_oracles(wl, streams):
+    return {s: OracleChain(wl, (lambda s_: (lambda f: embeddings(wl, s_, f)))(s),
+                           lambda l: projection(wl, l)) for s in streams}
+
+
+def _check_chain_frame(wl, fds, oracles, f, streams):
+    """Runs frame f on the GPU chain and compares every stored layer output of
+    the given streams with the float64 chain (each side feeds its own outputs
+    forward: nothing is teacher-forced).  Returns the worst error."""
+    x = torch.from_numpy(np.stack([embeddings(wl, s, f) for s in range(wl.streams)])).cuda()
+    keep = []
+    fds.frame(f, x, keep)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for s in streams:
+        outs, xl = oracles[s].frame(f)
+        errs = [float(np.abs(keep[layer][s].float().cpu().numpy() - outs[layer]).max())
+                for layer in range(wl.chain_layers)]
+        mags = [float(np.abs(outs[layer]).max()) for layer in range(wl.chain_layers)]
+        dx = float(np.abs(x[s].cpu().numpy() - xl).max())
+        print(f"frame {f} stream {s}: per-layer max err {np.round(errs, 4).tolist()}")
+        print(f"   per-layer max|O| {np.round(mags, 2).tolist()}  max|x_L - oracle| {dx:.4f}")
+        # every stored layer output (bf16) within the bf16 bar; x_L is the fp32
+        # sum of x_0 and these outputs, so the per-layer outputs are the gate
+        assert max(errs) <= BF16_TOL, (f, s, errs)
+        worst = max(worst, max(errs))
+    return worst
+
+
 def test_full_depth_chain_first_frames():
     """The 24-layer, 4-stream chain (hidden 1024, weights N(0, 0.02)) on its
     first frames, every output of streams 0 and 3 against the float64 chain."""
-    from rope_paged_kv_amd.chain import FullDepthStream
     wl = WORKLOADS[4]
-    weights = [to_dev(projection(wl, l), torch.bfloat16) for l in range(wl.chain_layers)]
-    fds = FullDepthStream(streams=wl.streams, layers=wl.chain_layers, heads=wl.heads,
-                          grid_h=wl.grid_h, grid_w=wl.grid_w, scale_frames=wl.scale_frames,
-                          sliding_window=wl.sliding_window, keyframe_interval=wl.keyframe_interval,
-                          frames=wl.frames, weights=weights)
-    oracles = {s: OracleChain(wl, (lambda s_: (lambda f: embeddings(wl, s_, f)))(s),
-                              lambda l: projection(wl, l)) for s in (0, 3)}
+    fds = _chain(wl)
+    oracles = _chain_oracles(wl, (0, 3))
     worst = 0.0
     for f in range(3):
-        x = torch.from_numpy(np.stack([embeddings(wl, s, f) for s in range(wl.streams)])).cuda()
-        keep = []
-        fds.frame(f, x, keep)
-        torch.cuda.synchronize()
-        for s in (0, 3):
-            if s == 3 and f == 2:
-                continue
-            outs, xl = oracles[s].frame(f)
-            errs = [np.abs(keep[layer][s].float().cpu().numpy() - outs[layer]).max()
-                    for layer in range(wl.chain_layers)]
-            mags = [np.abs(outs[layer]).max() for layer in range(wl.chain_layers)]
-            d = x[s].cpu().numpy() - xl
-            e, rms = np.abs(d).max(), np.sqrt(np.mean(d * d))
-            print(f"frame {f} stream {s}: per-layer max err {np.round(errs, 4).tolist()}")
-            print(f"   per-layer max|O| {np.round(mags, 2).tolist()}  max|x24| {np.abs(xl).max():.2f}"
-                  f"  max err {e:.4f}  rms err {rms:.2e}")
-            worst = max(worst, e)
-            # every stored layer output (bf16) within the bf16 bar
-            assert max(errs) <= BF16_TOL, (f, s, errs)
-            # x_24 is the fp32 sum of 24 stored bf16 outputs, each of which may
-            # round one bf16 ulp of its magnitude the other way: bound the sum
-            # by twice the sum of those ulps (margin for the propagation through
-            # the later layers); its rms by the rms of independent one-ulp
-            # differences in every layer.
-            ulps = np.array([2.0 ** (np.floor(np.log2(m)) - 7) for m in mags])
-            assert e <= 2 * ulps.sum(), (f, s, e, 2 * ulps.sum())
-            assert rms <= np.sqrt((ulps ** 2).sum()), (f, s, rms)
-    print(f"full-depth chain: max|x_24 - oracle| {worst:.3e}")
+        worst = max(worst, _check_chain_frame(wl, fds, oracles, f, (0, 3) if f < 2 else (0,)))
+    print(f"full-depth chain, frames 0-2: max|O_l - oracle| {worst:.3e}")
+
+
+def test_full_depth_structure_through_eviction_and_recycle():
+    """The full-depth stack's structure at a reduced size (4 streams, 24
+    alternating frame / global layers, fused projection + RoPE + append,
+    keyframe every 2nd frame, scale_frames 2, window 3; 6x6 grid, 4 heads,
+    hidden 256): all 16 frames, every layer's output of every stream against
+    the float64 chain -- past the first eviction (frame 10) and the first
+    recycled page (frame 12).  The global caches' bookkeeping then matches the
+    page simulator."""
+    from rpkv_inputs import small_variants
+    wl = small_variants()["small_depth"]
+    fds = _chain(wl)
+    oracles = _chain_oracles(wl, range(wl.streams))
+    sim = pages.PageSim(wl.scale_frames, wl.sliding_window, wl.special_page_size, wl.n_special)
+    worst = 0.0
+    for f in range(wl.frames):
+        sim.append(f, wl.is_keyframe(f))
+        worst = max(worst, _check_chain_frame(wl, fds, oracles, f, range(wl.streams)))
+        sim.evict()
+        if f in (10, 12):
+            for layer in (0, wl.chain_layers // 2 - 1):
+                for s in range(wl.streams):
+                    st = fds.global_cache.state(layer, s)
+                    assert st["free_list"] == sim.free and st["window_pages"] == list(sim.window), (f, layer, s)
+    assert sim.fresh == wl.scale_frames + wl.sliding_window + 1 and len(sim.free) == 1
+    print(f"reduced full-depth chain, 16 frames: max|O_l - oracle| {worst:.3e}")
