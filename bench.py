@@ -1,22 +1,28 @@
 """Benchmark of the per-frame hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline]
+    python bench.py --append-only [--workload W]
 
 One step is one pass of the whole path over one synthetic stream: reset the
-cache, then for every frame RoPE + append (kv_append_frame), paged attention
-(attend_frame) and deferred eviction (kv_evict_deferred).  The default
-workload is the single-layer bf16 stream of 64 frames of 37x37 patches + 6
-special tokens, 16 heads of 64, scale_frames 8, sliding_window 16, every frame
-a keyframe.  --workload 0/2/3 select the other single-layer streams, --workload
-4 the full-depth stack (4 streams x 24 layers alternating frame and global
-attention, the fused QKV projection + RoPE + append (kv_project_append_frame)
-and the fp32 residual included; value counts stream-frames).  All inputs are generated (seeded, N(0,1), rounded to bf16)
-and copied to HBM before timing.
+caches, then for every frame RoPE + append, paged attention (attend_frame)
+and deferred eviction (kv_evict_deferred).  The default workload (4) is the
+full-depth stack, the largest single-GPU workload of 37x37-patch frames: 4
+streams of 256 frames (37x37 patches + 6 special tokens, 16 heads of 64,
+bf16), 24 layers alternating frame attention (the frame's own tokens) and
+global attention over the paged cache (scale_frames 8, sliding_window 32,
+keyframe every 2nd frame), each layer's fused QKV projection + RoPE + append
+(kv_project_append_frame, hidden 1024) and the fp32 residual included; value
+counts stream-frames.  --workload 0..3 select the single-layer streams (RoPE +
+append by kv_append_frame).  All inputs are generated (seeded, N(0,1), rounded
+to bf16) and copied to HBM before timing.
 
 Prints one JSON line: value = frames/s over the K timed steps; roofline of the
 dominant kernel (paged attention, matrix-core bound) from HIP events recorded
 around every attend_frame launch in the timed region; cpu_baseline = the CPU
 oracle on a bounded sample of the same stream.
+
+--append-only times kv_append_frame alone (RoPE + page write, HBM bound) at
+the workload's geometry, all its streams in one launch, and prints its GB/s.
 """
 from __future__ import annotations
 
@@ -80,11 +86,27 @@ def read_traffic(workload):
 
 
 def cpu_threads():
+    """Threads of the BLAS pool numpy runs its products on (the oracle's
+    parallel part; its exponentials run on one thread)."""
     try:
         from threadpoolctl import threadpool_info
         return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         return 1
+
+
+def cpu_host():
+    """CPU model and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "host_cores_available": len(os.sched_getaffinity(0))}
 
 
 def cpu_baseline(wl, budget_s=20.0):
@@ -106,10 +128,11 @@ def cpu_baseline(wl, budget_s=20.0):
     return {"value": done * wl.streams / dt, "unit": "frames/s", "cores": int(cpu_threads()),
             "kind": "oracle",
             "sample": f"frames {start}..{start + done - 1} of one stream (full window, all {wl.heads} "
-                      f"heads, all {wl.tokens} query rows), float64 numpy, past frames' K/V pre-rotated"}
+                      f"heads, all {wl.tokens} query rows), float64 numpy, past frames' K/V pre-rotated",
+            **cpu_host()}
 
 
-def cpu_baseline_chain(wl, frames=2):
+def cpu_baseline_chain(wl, frames=3):
     """The full-depth oracle chain on the first frames of one stream."""
     from oracle.chain import OracleChain
     from rpkv_inputs import embeddings, projection
@@ -122,7 +145,8 @@ def cpu_baseline_chain(wl, frames=2):
     return {"value": frames / dt, "unit": "stream-frames/s", "cores": int(cpu_threads()),
             "kind": "oracle",
             "sample": f"frames 0..{frames - 1} of stream 0 through all {wl.chain_layers} layers "
-                      f"(projection, RoPE, attention, residual), float64 numpy"}
+                      f"(projection, RoPE, attention, residual), float64 numpy",
+            **cpu_host()}
 
 
 def result_line(wl, args, elapsed, frames_per_step, att_ms, att_flops, app_ms, info_splits,
@@ -298,12 +322,70 @@ def bench_full_depth(wl, args, dev):
     return res
 
 
+def bench_append(wl, args, dev):
+    """kv_append_frame alone at the workload's geometry (all streams in one
+    launch): GB/s of its algorithmic bytes, from HIP events around each call."""
+    import numpy as np
+    import torch
+
+    import rope_paged_kv_amd as rp
+    from rpkv_inputs import frame_qkv
+
+    nf = 16
+    qkv = [tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in frame_qkv(wl, 0, f))
+           for f in range(nf)]
+    spec = rp.make_spec(pairs=wl.pairs, theta=wl.theta, ntk_factor=wl.ntk_factor,
+                        max_frames=wl.t_rows, max_h=wl.grid_h, max_w=wl.grid_w, layout=wl.rope_layout)
+    cfg = rp.make_config(num_layers=1, num_streams=wl.streams, num_heads=wl.heads,
+                         grid_h=wl.grid_h, grid_w=wl.grid_w, dtype=wl.dtype,
+                         patch_page_size=wl.page_size, special_page_size=wl.special_page_size,
+                         scale_frames=wl.scale_frames, sliding_window=wl.sliding_window,
+                         max_keyframes=wl.n_keyframes(), rope=spec)
+    cache = rp.PagedKVCache(cfg, device=dev)
+    q_rot = torch.empty_like(qkv[0][0])
+    F = wl.frames
+
+    def one_pass(ev=None):
+        cache.reset(0)
+        for f in range(F):
+            q, k, v = qkv[f % nf]
+            if ev is not None:
+                ev[f][0].record()
+            cache.append(0, f, int(wl.is_keyframe(f)), q, k, v, q_rot)
+            if ev is not None:
+                ev[f][1].record()
+            cache.evict(0)
+
+    for _ in range(args.warmup):
+        one_pass()
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(F)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        one_pass(events[k])
+    torch.cuda.synchronize()
+    us = float(np.mean([[e[f][0].elapsed_time(e[f][1]) for f in range(F)] for e in events])) * 1e3
+    gbs = append_bytes(wl) / us / 1e3
+    return {"metric": "kv_append_frame GB/s (RoPE + page write, % HBM)", "value": round(gbs, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "dtype": wl.dtype, "data": "synthetic",
+            "config": {"workload": wl.name, "streams": wl.streams,
+                       "grid": f"{wl.grid_h}x{wl.grid_w}", "heads": wl.heads,
+                       "frames_per_step": F},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "avg_launch_us": round(us, 2),
+                         "algorithmic_bytes_per_launch": append_bytes(wl)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--workload", type=int, default=4, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--append-only", action="store_true",
+                    help="time kv_append_frame alone at the workload's geometry")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
@@ -331,7 +413,9 @@ def main():
 
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    if wl.chain_layers:
+    if args.append_only:
+        res = bench_append(wl, args, dev)
+    elif wl.chain_layers:
         res = bench_full_depth(wl, args, dev)
     else:
         res = bench_single_layer(wl, args, dev)
