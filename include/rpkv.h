@@ -59,7 +59,8 @@ enum {
     RPKV_EINVAL = -1,   /* bad argument, shape, alignment or layer index */
     RPKV_EHIP = -2,     /* a HIP runtime call failed */
     RPKV_ENOSPACE = -3, /* patch pool or special stream exhausted (device status) */
-    RPKV_ESTATE = -4    /* call not valid in the handle's current state */
+    RPKV_ESTATE = -4,   /* call not valid in the handle's current state */
+    RPKV_ETOOBIG = -5   /* request larger than the library's static scratch */
 };
 
 enum { RPKV_BF16 = 0, RPKV_F32 = 1 };
@@ -275,6 +276,23 @@ int kv_project_append_frame_grid(kv_handle* h, int layer, int frame_idx, int com
  * softmax); fp32 runs in fp32 throughout.
  */
 int attend_frame(kv_handle* h, int layer, const void* q_rot, void* out, float* lse, void* stream);
+
+/*
+ * attend_frame for callers that cannot allocate device memory or take a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, kernels and results as
+ * attend_frame (bit for bit); the split partial outputs go to a static array
+ * inside the library instead of the handle's memory, and the call allocates
+ * nothing.  Limit: a handle whose split scratch, S*H*splits*N*136 bytes
+ * (rounded up), exceeds RPKV_STATIC_SCRATCH_BYTES gets RPKV_ETOOBIG; with one
+ * split nothing is used.  The array is per GPU, held by every process that
+ * loads the library until it ends, and shared by every call on that GPU:
+ * calls that may run at the same time on one GPU (other streams, other
+ * threads) race on it and must be ordered by the caller.
+ */
+#define RPKV_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+int attend_frame_noalloc(kv_handle* h, int layer, const void* q_rot, void* out, float* lse,
+                         void* stream);
 
 /* Deferred eviction for `layer` ([KVB] "Memory-Efficient Sliding Window
  * Management", "Dynamic Keyframe Selection"; [ROPE-KV] "Dual-Stream Memory

@@ -30,8 +30,8 @@ import ctypes as C
 from typing import Optional
 
 from . import _abi
-from ._abi import (RPKV_BF16, RPKV_EHIP, RPKV_EINVAL, RPKV_ENOSPACE, RPKV_ESTATE, RPKV_F32,
-                   RPKV_OK, KvConfig, Rope3dSpec)
+from ._abi import (RPKV_BF16, RPKV_EHIP, RPKV_EINVAL, RPKV_ENOSPACE, RPKV_ESTATE, RPKV_ETOOBIG,
+                   RPKV_F32, RPKV_OK, RPKV_STATIC_SCRATCH_BYTES, KvConfig, Rope3dSpec)
 
 _lib = _abi.load()
 
@@ -112,6 +112,11 @@ def kv_project_append_frame_grid(h, layer: int, frame_idx: int, commit: int, gri
 
 def attend_frame(h, layer: int, q_rot, out, lse, stream: int) -> None:
     _check(_lib.attend_frame(h, layer, _vp(q_rot), _vp(out), _vp(lse), stream), "attend_frame")
+
+
+def attend_frame_noalloc(h, layer: int, q_rot, out, lse, stream: int) -> None:
+    _check(_lib.attend_frame_noalloc(h, layer, _vp(q_rot), _vp(out), _vp(lse), stream),
+           "attend_frame_noalloc")
 
 
 def kv_evict_deferred(h, layer: int, stream: int) -> None:
@@ -259,6 +264,15 @@ class PagedKVCache:
         self._expect("lse", lse, (c.num_streams, c.num_heads, c.special_tokens + c.grid_h * c.grid_w),
                      self.torch.float32)
         attend_frame(self.h, layer, q_rot, out, lse, self.stream)
+
+    def attend_noalloc(self, layer, q_rot, out, lse=None):
+        """attend_frame_noalloc: the split partials in the library's static scratch."""
+        self._act("q_rot", q_rot)
+        self._act("out", out)
+        c = self.cfg
+        self._expect("lse", lse, (c.num_streams, c.num_heads, c.special_tokens + c.grid_h * c.grid_w),
+                     self.torch.float32)
+        attend_frame_noalloc(self.h, layer, q_rot, out, lse, self.stream)
 
     def evict(self, layer):
         kv_evict_deferred(self.h, layer, self.stream)

@@ -4,7 +4,8 @@ from __future__ import annotations
 import ctypes as C
 import os
 
-RPKV_OK, RPKV_EINVAL, RPKV_EHIP, RPKV_ENOSPACE, RPKV_ESTATE = 0, -1, -2, -3, -4
+RPKV_OK, RPKV_EINVAL, RPKV_EHIP, RPKV_ENOSPACE, RPKV_ESTATE, RPKV_ETOOBIG = 0, -1, -2, -3, -4, -5
+RPKV_STATIC_SCRATCH_BYTES = 128 << 20
 RPKV_BF16, RPKV_F32 = 0, 1
 RPKV_MAX_POOL_PAGES = 512
 
@@ -12,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librpkv.so"
 
 EXPORTS = ("rope3d_tables_bytes", "rope3d_build_tables", "kv_required_bytes", "kv_create",
            "kv_destroy", "kv_reset", "kv_append_frame", "kv_append_frame_grid", "kv_project_append_frame", "kv_project_append_frame_grid", "attend_frame",
-           "kv_evict_deferred",
+           "attend_frame_noalloc", "kv_evict_deferred",
            "kv_rollback", "kv_read_state", "kv_get_info", "rpkv_strerror")
 
 
@@ -81,6 +82,7 @@ def load() -> C.CDLL:
         "kv_project_append_frame": (i, [vp, i, i, i, vp, i, vp, vp, vp, vp]),
         "kv_project_append_frame_grid": (i, [vp, i, i, i, i, i, vp, i, vp, vp, vp, vp]),
         "attend_frame": (i, [vp, i, vp, vp, vp, vp]),
+        "attend_frame_noalloc": (i, [vp, i, vp, vp, vp, vp]),
         "kv_evict_deferred": (i, [vp, i, vp]),
         "kv_rollback": (i, [vp, i, vp]),
         "kv_read_state": (i, [vp, i, i, C.POINTER(KvStateHost), vp]),

@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "rpkv_internal.h"
@@ -131,6 +132,46 @@ bool layout(const kv_config* c, Layout* L) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? RPKV_OK : RPKV_EHIP; }
 
+// Split scratch of attend_frame_noalloc, for callers that cannot allocate:
+// the partial outputs and their (LSE, factor) pairs live in this array
+// instead of the handle's memory.  Every GPU the library runs on holds its own
+// copy until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it stands for a host-side shadow, not a device address):
+// the device address is looked up once per device, with that device current,
+// and kept in scratch_ptr.  Every call on a GPU shares that GPU's copy, so
+// calls that overlap on one GPU race.  Nothing in it needs clearing: each
+// call writes every row its merge reads.
+static __device__ __align__(256) char scratch[RPKV_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+char* scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (resolved on first use).
+hipError_t current_scratch(char** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        scratch_ptr[dev] = (char*)p;
+    }
+    *out = scratch_ptr[dev];
+    return hipSuccess;
+}
+
+// Bytes of split scratch one attend_frame call of this layout uses: fp16
+// partial outputs, then (LSE, factor) pairs.
+size_t split_scratch_bytes(const Layout& L, size_t* off_ls) {
+    const size_t parts = L.splits > 1 ? (size_t)L.S * L.H * L.splits * L.N : 0;
+    *off_ls = round_up(parts * kHeadDim * 2, 256);
+    return *off_ls + round_up(parts * 8, 256);
+}
+
 CacheState* states_of(kv_handle* h, int layer) {
     return (CacheState*)(h->base + h->L.off_state) + (size_t)layer * h->L.S;
 }
@@ -192,7 +233,10 @@ int kv_create(const kv_config* cfg, void* d_mem, size_t bytes, void* stream, kv_
     h->appended = h->committed = 0;
     h->pending0 = false;
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e = launch_fill_zero(d_mem, L.total, st);
+    // Library set-up on this device: the static split scratch's address.
+    char* scr = nullptr;
+    hipError_t e = current_scratch(&scr);
+    if (e == hipSuccess) e = launch_fill_zero(d_mem, L.total, st);
     if (e == hipSuccess) e = launch_reset(states_of(h, 0), cfg->num_layers * L.S, st);
     if (e != hipSuccess) {
         delete h;
@@ -331,9 +375,8 @@ int kv_project_append_frame_grid(kv_handle* h, int layer, int frame_idx, int com
     return rc;
 }
 
-int attend_frame(kv_handle* h, int layer, const void* q_rot, void* out, float* lse, void* stream) {
-    if (!h || layer < 0 || layer >= h->cfg.num_layers || !q_rot || !out) return RPKV_EINVAL;
-    if (!aligned16(q_rot) || !aligned16(out) || ((uintptr_t)lse & 3)) return RPKV_EINVAL;
+// Attention arguments of one call; the split scratch is set by the caller.
+static AttnArgs attend_args(kv_handle* h, int layer, const void* q_rot, void* out, float* lse) {
     const Layout& L = h->L;
     AttnArgs a;
     a.q = q_rot;
@@ -347,8 +390,6 @@ int attend_frame(kv_handle* h, int layer, const void* q_rot, void* out, float* l
     a.vsp = h->base + L.off_vsp + caches_before * L.ksp_elems * L.elem;
     a.kpool_elems = L.kpool_elems;
     a.ksp_elems = L.ksp_elems;
-    a.part_o = (uint16_t*)(h->base + L.off_part_o);
-    a.part_ls = (float2*)(h->base + L.off_part_ls);
     a.S = L.S;
     a.N = L.N;
     a.H = L.H;
@@ -362,6 +403,29 @@ int attend_frame(kv_handle* h, int layer, const void* q_rot, void* out, float* l
     a.n_logical = L.q_tiles * L.H * L.S * L.splits;
     a.scale = 1.0f / sqrtf((float)kHeadDim);
     a.scale_log2 = (float)(1.0 / sqrt((double)kHeadDim) * 1.4426950408889634);
+    return a;
+}
+
+int attend_frame(kv_handle* h, int layer, const void* q_rot, void* out, float* lse, void* stream) {
+    if (!h || layer < 0 || layer >= h->cfg.num_layers || !q_rot || !out) return RPKV_EINVAL;
+    if (!aligned16(q_rot) || !aligned16(out) || ((uintptr_t)lse & 3)) return RPKV_EINVAL;
+    AttnArgs a = attend_args(h, layer, q_rot, out, lse);
+    a.part_o = (uint16_t*)(h->base + h->L.off_part_o);
+    a.part_ls = (float2*)(h->base + h->L.off_part_ls);
+    return hip_status(launch_attend(a, h->cfg.dtype, (hipStream_t)stream));
+}
+
+int attend_frame_noalloc(kv_handle* h, int layer, const void* q_rot, void* out, float* lse,
+                         void* stream) {
+    if (!h || layer < 0 || layer >= h->cfg.num_layers || !q_rot || !out) return RPKV_EINVAL;
+    if (!aligned16(q_rot) || !aligned16(out) || ((uintptr_t)lse & 3)) return RPKV_EINVAL;
+    size_t off_ls = 0;
+    if (split_scratch_bytes(h->L, &off_ls) > RPKV_STATIC_SCRATCH_BYTES) return RPKV_ETOOBIG;
+    char* scr = nullptr;
+    if (current_scratch(&scr) != hipSuccess) return RPKV_EHIP;
+    AttnArgs a = attend_args(h, layer, q_rot, out, lse);
+    a.part_o = (uint16_t*)scr;
+    a.part_ls = (float2*)(scr + off_ls);
     return hip_status(launch_attend(a, h->cfg.dtype, (hipStream_t)stream));
 }
 
@@ -455,6 +519,7 @@ const char* rpkv_strerror(int code) {
         case RPKV_EHIP: return "HIP runtime error";
         case RPKV_ENOSPACE: return "cache pool or special stream exhausted";
         case RPKV_ESTATE: return "invalid state";
+        case RPKV_ETOOBIG: return "split scratch larger than the library's static scratch";
         default: return "unknown error";
     }
 }
