@@ -29,6 +29,11 @@ from __future__ import annotations
 import ctypes as C
 from typing import Optional
 
+# torch first: the library must bind to the HIP runtime torch carries.  Loaded
+# before torch, it would pull in the system runtime, and torch's device
+# pointers and streams would belong to another runtime instance.
+import torch  # noqa: F401
+
 from . import _abi
 from ._abi import (RPKV_BF16, RPKV_EHIP, RPKV_EINVAL, RPKV_ENOSPACE, RPKV_ESTATE, RPKV_ETOOBIG,
                    RPKV_F32, RPKV_OK, RPKV_STATIC_SCRATCH_BYTES, KvConfig, Rope3dSpec)

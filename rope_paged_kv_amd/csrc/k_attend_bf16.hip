@@ -1,5 +1,5 @@
 // Paged attention of one frame's tokens over the visible page table, bf16 on
-// the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16), fp32 accumulation.
+// the gfx950 matrix cores, fp32 accumulation.
 //
 // What is computed (page "How 3D RoPE Positional Encoding Works with the Paged
 // KV Cache in LingBot-Map", section "Attention Computation with Cached RoPE";
@@ -14,27 +14,32 @@
 //    split of the visible key range; each wave owns 32 queries;
 //  * keys are walked in tiles of 64 that never straddle a page (a patch page
 //    of P tokens is ceil(P/64) tiles; the special stream, whose pages are
-//    appended in order and never evicted, is contiguous per head);
+//    appended in order and never evicted, is contiguous per head), each tile
+//    in two halves of 32 keys;
 //  * tiles stream from HBM straight into LDS (buffer_load ... lds: no staging
 //    registers, the page offset in a scalar register) through rings of 2 K
-//    and 3 V^T stages, one barrier per tile; 16-byte chunks are XOR-swizzled
-//    so operand reads hit 64 distinct banks (40 KB of LDS per workgroup);
-//  * scores are formed transposed, S^T = K Q^T (keys on the MFMA rows, queries
-//    on the columns): each lane holds 16 scores of one query per 32-key half
-//    tile, so the softmax statistics stay in-lane but for one exchange with
-//    the lane 32 apart; P^T rounded to bf16 is directly the B operand of
+//    and 2 V^T stages, one barrier per tile; 16-byte chunks are XOR-swizzled
+//    so operand reads hit 64 distinct banks;
+//  * scores are formed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16:
+//    keys on the rows, queries on the columns): each lane holds 16 scores of
+//    one query per half tile; P^T rounded to bf16 is directly the B operand of
 //    O^T = V^T P^T, V being stored transposed in the cache in the key order
 //    this layout produces;
-//  * the wave is software-pipelined by half tiles: the score products of the
-//    next half are issued before the exponentials of the current one, so the
-//    matrix core and the vector ALU work side by side (the next half of the
-//    last half tile of tile i is the first half of tile i+1, formed after the
-//    barrier of tile i+1);
-//  * scores s = q.k come out of the matrix core in fp32 from the stored bf16
-//    Q and K (no extra rounding of Q); one fused multiply-add per score turns
-//    s into the base-2 exponent t = s*log2(e)/sqrt(D) - M (M: the running
-//    reference max), and p = exp2(t) costs one transcendental; M moves (and
-//    the accumulated output is rescaled) only when a score exceeds it by 2^8;
+//  * software pipeline over half tiles: the step of half h issues the scores
+//    of half h+1 and the output products of half h-1 on the matrix core, and
+//    the softmax of half h on the vector ALU -- nothing in a step waits for
+//    another part of the same step, so the waves of a SIMD overlap one's
+//    matrix work with another's vector work;
+//  * the row sums l = sum p are formed on the matrix core too, from the same
+//    bf16 P^T operand (v_mfma_f32_16x16x32_bf16 against a 0/1 selection
+//    matrix, so numerator and denominator use the same rounded weights);
+//  * one fused multiply-add per score gives the base-2 exponent
+//    t = s*log2(e)/sqrt(D) - M from the fp32 score of the stored bf16 Q and K
+//    (no extra rounding of Q), and p = exp2(t); M sits 7 above the running
+//    max, so weights stay below 2^-7, and moves only when some weight reaches
+//    2, i.e. a score beats that max by 2^8 (checked on the packed bf16
+//    weights with a few bit operations instead of a max per score); the
+//    accumulated outputs and row sums are rescaled then;
 //  * several splits of the key range are merged by their log-sum-exp.
 #include "rpkv_internal.h"
 
@@ -43,20 +48,27 @@ namespace rpkv {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
+// Read-only during the kernel and read with uniform indices: loads through
+// this pointer go to the scalar cache (s_load), which leaves the vector
+// memory counter -- the one the tile loads are waited on with -- alone.
+typedef const int __attribute__((address_space(4)))* cint_ptr;
 
 constexpr int kWaves = 4;
 constexpr int kQW = 32;                          // queries per wave
 constexpr int kQB = kWaves * kQW;                // queries per workgroup
 constexpr int kTileBytes = kTile * kHeadDim * 2; // one 64x64 bf16 tile: 8 KB
 constexpr int kHalfBytes = 32 * 128;             // 32 rows of a tile
-// LDS rings: K tiles in 2 stages, V^T tiles in 3.  K of tile i is read from
-// the barrier of tile i up to the barrier of tile i+1, V^T of tile i up to
-// the barrier of tile i+2; tile i+2 is loaded from the barrier of tile i+1.
-constexpr int kKStages = 2, kVStages = 3;
-constexpr int kGroup = 6;                        // tiles per unrolled group (lcm of the rings)
-constexpr int kLdsBytes = (kKStages + kVStages) * kTileBytes;
+// LDS rings of 3 stages for K and for V^T.  K of tile i is read by the steps
+// of halves (i-1, 1) and (i, 0) (scores one half ahead), V^T of tile i by the
+// steps of halves (i, 1) and (i+1, 0) (output products one half behind); the
+// barrier after half (i, 0) frees the stages of K(i) and V^T(i-1), which then
+// take K(i+3) and V^T(i+2): every tile load has two tiles of work to land in.
+// The tile loop is unrolled by three, so every stage offset is a constant.
+constexpr int kStages = 3;
 // Word 3 of a raw (unstructured) buffer resource on gfx9: 32-bit data format.
 constexpr int kBufWord3 = 0x00020000;
 
@@ -80,39 +92,90 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_over(const char* p, size_t bytes
     return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, kBufWord3);
 }
 
+// A walk over the key tiles of one split, one tile at a time (all scalar):
+// patch tiles page by page through the visible table (the page id read once
+// per page), then the special stream's tiles.  The number of patch tiles npt
+// and tiles per page tpp are the split's (passed in, not stored).
+// (readfirstlane keeps every field in scalar registers: the integer
+// division would otherwise come back in a vector register, and the page id
+// with it, turning each tile load into a loop over lanes.)
+struct TileWalk {
+    int t, pi, tip, page;
+    __device__ void init(int t0, int npt, int tpp, cint_ptr vis) {
+        t = uniform(t0);
+        pi = uniform(t / tpp);
+        tip = uniform(t - pi * tpp);
+        page = t < npt ? uniform(vis[pi]) : 0;
+    }
+    // returns true when the walk enters a new patch page
+    __device__ bool next(int npt, int tpp, cint_ptr vis) {
+        ++t;
+        if (++tip == tpp) {
+            tip = 0;
+            ++pi;
+            if (t < npt) {
+                page = uniform(vis[pi]);
+                return true;
+            }
+        }
+        return false;
+    }
+};
+
+// Two 16-byte-per-lane tile loads straight into LDS (rows 8 apart: LDS
+// addresses lds0 and lds0 + 1024), written as one asm statement so that the
+// compiler does not track them: it would otherwise wait for them before
+// operand reads of other stages it cannot tell apart.  The tile loop orders
+// them itself (s_waitcnt vmcnt(0) and a barrier before any read of the stage
+// they fill).  M0 carries the LDS address of an LDS DMA; it is saved and
+// restored around the loads, with the wait states a write of M0 needs before
+// such a load.  The loads write no VGPR.
+__device__ inline void dma_pair(__amdgpu_buffer_rsrc_t r, const char* lds0, uint32_t voff0, uint32_t voff1,
+                                uint32_t soff) {
+    const uint32_t a0 = (uint32_t)uniform((int)(uint32_t)(uintptr_t)lds0);
+    const uint32_t a1 = a0 + 1024u;
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 1\n\t"
+        "buffer_load_dwordx4 %3, %5, %6 offen lds\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 1\n\t"
+        "buffer_load_dwordx4 %4, %5, %6 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(a0), "s"(a1), "v"(voff0), "v"(voff1), "s"(r), "s"(soff)
+        : "memory");
+}
+
 // Loads of one (stream, head): buffer resources over its K pool, V^T pool and
 // special K / V^T, and this lane's byte offsets inside the 8-row slabs it
 // loads (its row, and the 16-byte chunk that belongs at its slot under the
-// swizzle).  All page arithmetic is scalar.
+// swizzle).  A wave loads rows 16*wave .. 16*wave+15 of a tile, 8 rows per
+// load.
 struct Loader {
     __amdgpu_buffer_rsrc_t kpool, vpool, ksp, vsp;
-    const int* vis;          // visible pages (read through the scalar cache)
-    int vis_n, tpp, slot_cap;
+    cint_ptr vis;            // visible pages
+    int slot_cap;
     uint32_t lk0, lk1, lvp0, lvp1, lvs0, lvs1;
 
-    // Issues this wave's share of tile t (rows 16*wave .. 16*wave+15 of the K
-    // tile and of the V^T tile, 8 rows per instruction) into an LDS stage.
-    __device__ void issue(int t, char* kstage, char* vstage, int wave) const {
-        char* k0 = kstage + wave * 2 * 8 * 128;
-        char* v0 = vstage + wave * 2 * 8 * 128;
-        const int npt = vis_n * tpp;
-        if (t < npt) {
-            const int pi = t / tpp;
-            const uint32_t off = (uint32_t)(t - pi * tpp) * kTile;
-            const uint32_t page = (uint32_t)uniform(vis[pi]);
-            const uint32_t ko = (page * (uint32_t)slot_cap + off) * 128u;
-            const uint32_t vo = page * (uint32_t)slot_cap * 128u + off * 2u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kpool, (lds_void_ptr)k0, 16, lk0, ko, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kpool, (lds_void_ptr)(k0 + 1024), 16, lk1, ko, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vpool, (lds_void_ptr)v0, 16, lvp0, vo, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vpool, (lds_void_ptr)(v0 + 1024), 16, lvp1, vo, 0, 0);
+    __device__ void issue_k(const TileWalk& w, int npt, char* stage, int wave) const {
+        const char* d = stage + wave * 2 * 8 * 128;
+        if (w.t < npt) {
+            const uint32_t ko = ((uint32_t)w.page * (uint32_t)slot_cap + (uint32_t)w.tip * kTile) * 128u;
+            dma_pair(kpool, d, lk0, lk1, ko);
         } else {
-            const uint32_t off = (uint32_t)(t - npt) * kTile;
-            const uint32_t ko = off * 128u, vo = off * 2u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksp, (lds_void_ptr)k0, 16, lk0, ko, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksp, (lds_void_ptr)(k0 + 1024), 16, lk1, ko, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vsp, (lds_void_ptr)v0, 16, lvs0, vo, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vsp, (lds_void_ptr)(v0 + 1024), 16, lvs1, vo, 0, 0);
+            dma_pair(ksp, d, lk0, lk1, (uint32_t)(w.t - npt) * kTile * 128u);
+        }
+    }
+    __device__ void issue_v(const TileWalk& w, int npt, char* stage, int wave) const {
+        const char* d = stage + wave * 2 * 8 * 128;
+        if (w.t < npt) {
+            const uint32_t vo = (uint32_t)w.page * (uint32_t)slot_cap * 128u + (uint32_t)w.tip * kTile * 2u;
+            dma_pair(vpool, d, lvp0, lvp1, vo);
+        } else {
+            dma_pair(vsp, d, lvs0, lvs1, (uint32_t)(w.t - npt) * kTile * 2u);
         }
     }
 };
@@ -120,10 +183,9 @@ struct Loader {
 // Running state of one wave's 32 queries.
 struct Acc {
     f32x16 o0, o1;     // O^T, d rows 0-31 and 32-63
-    float lp[4];       // partial row sums
-    float M;           // reference max of the base-2 exponents
+    f32x4 rs;          // row sums: lanes 0-15 hold those of queries lane (rs[0]) and lane+16 (rs[1])
+    float M;           // reference max of the base-2 exponents (shared by lanes l and l^32)
     float c;           // log2(e)/sqrt(D)
-    bool first;
 };
 
 // s = q.k for the 32 keys of half kb of a tile (rows 32*kb + col of the K
@@ -142,102 +204,98 @@ __device__ __forceinline__ f32x16 scores(const char* tile, int kb, const int* fo
     return s;
 }
 
-// One half tile: the softmax weights of sc (half kb of `tile`, len valid keys
-// in the tile), their output products, and -- interleaved with them, so the
-// matrix core works while the exponentials run -- the scores of the next half
-// tile into nxt (K rows at knext; the caller makes sure they are loaded, or
-// ignores nxt).  Key of sc[r]: 32*kb + 8*(r/4) + 4*hh + r%4; its V^T column
-// sits at that key's slot, chunk 4*kb + 2*(r/8) + hh.
-__device__ __forceinline__ void step(f32x16& sc, f32x16& nxt, const char* vt, int kb, int len,
-                                     const char* knext, const int* foff, const bf16x8* qf, int hh,
-                                     Acc& A) {
-    if (len < 32 * kb + 32) {   // ragged: keys past the tile's end do not count
-        const int lim = len - 32 * kb - 4 * hh;
+// Output products and row sums of a half whose bf16 weights are pp (V^T rows
+// of half vkb of the tile at vt).
+__device__ __forceinline__ void products(const bf16x8 (&pp)[2], const char* vt, int vkb, const int* foff,
+                                         const bf16x8& sel, Acc& A) {
+    bf16x8 v[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        v[m][0] = *(const bf16x8*)(vt + foff[2 * vkb + m]);
+        v[m][1] = *(const bf16x8*)(vt + kHalfBytes + foff[2 * vkb + m]);
+    }
+    A.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[0][0], pp[0], A.o0, 0, 0, 0);
+    A.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[0][1], pp[0], A.o1, 0, 0, 0);
+    A.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[1][0], pp[1], A.o0, 0, 0, 0);
+    A.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[1][1], pp[1], A.o1, 0, 0, 0);
+    A.rs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pp[0], A.rs, 0, 0, 0);
+    A.rs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pp[1], A.rs, 0, 0, 0);
+}
+
+// p = exp2(s*c - M) of the 16 scores, rounded to bf16 and packed as the two
+// 16-key operand blocks of the half (keys 0-15 from sc[0..7], 16-31 from
+// sc[8..15]).
+__device__ __forceinline__ void weights(const f32x16& sc, float c, float M, bf16x8 (&pn)[2]) {
+    bf16x2 pr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const f32x2 x = {__builtin_amdgcn_exp2f(fmaf(sc[2 * e], c, -M)),
+                         __builtin_amdgcn_exp2f(fmaf(sc[2 * e + 1], c, -M))};
+        pr[e] = __builtin_convertvector(x, bf16x2);
+    }
+    pn[0] = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
+                                    __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    pn[1] = __builtin_shufflevector(__builtin_shufflevector(pr[4], pr[5], 0, 1, 2, 3),
+                                    __builtin_shufflevector(pr[6], pr[7], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// One pipeline step: the softmax weights pn of the half whose scores are sc
+// (rag: a ragged half, whose keys at or past lim -- its valid count minus
+// 4*hh -- do not count), the scores sn of the next half (K rows at knext) and
+// the output products of the previous half (weights pp, V^T half vkb of the
+// tile at vprev).  Key of sc[r]: 8*(r/4) + 4*hh + r%4 within the half.
+__device__ __forceinline__ void step(f32x16& sc, f32x16& sn, bf16x8 (&pn)[2], const bf16x8 (&pp)[2],
+                                     const char* knext, const char* vprev, int vkb, bool rag, int lim,
+                                     const int* foff, const bf16x8* qf, const bf16x8& sel, Acc& A) {
+    if (rag) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             if (8 * (r >> 2) + (r & 3) >= lim) sc[r] = -INFINITY;
     }
-    const float ma = max3f(sc[0], sc[1], sc[2]);
-    const float mb = max3f(sc[3], sc[4], sc[5]);
-    const float mc = max3f(sc[6], sc[7], sc[8]);
-    const float md = max3f(sc[9], sc[10], sc[11]);
-    const float me = max3f(sc[12], sc[13], sc[14]);
-    const float mx = max3f(max3f(ma, mb, mc), fmaxf(md, me), sc[15]);
-    // (A half with no valid key -- a tile past a short page's tokens -- has
-    // every score at -inf: it moves nothing and adds nothing.)
-    if ((A.first && __any(mx > -INFINITY)) || __any(fmaf(mx, A.c, -A.M) > 8.f)) {
-        // rare: move M (jointly for both lanes of a query; never down after
-        // the first half tile) and rescale what was accumulated.
-        const float d = fmaxf(mx, __shfl_xor(mx, 32)) * A.c;
-        const float m_new = A.first ? d : fmaxf(d, A.M);
-        const float alpha = A.first ? 0.f : __builtin_amdgcn_exp2f(A.M - m_new);
-        A.first = false;
+    sn = scores(knext, 0, foff, qf);
+    products(pp, vprev, vkb, foff, sel, A);
+    weights(sc, A.c, A.M, pn);
+    // M is kept 7 above the largest exponent seen when it last moved, so the
+    // weights stay below 2^-7 until a score exceeds that max by 8 (base 2).
+    // Some weight >= 2 (bf16 exponent field >= 128: its top bit set), or the
+    // first valid keys against the initial M: move M to 7 above this half's
+    // max (jointly for the two lanes of a query; never down), rescale what
+    // was accumulated -- including the products just issued, which used the
+    // old M -- and form the weights again.
+    const u32x4 w0 = __builtin_bit_cast(u32x4, pn[0]);
+    const u32x4 w1 = __builtin_bit_cast(u32x4, pn[1]);
+    const uint32_t any = (w0[0] | w0[1] | w0[2]) | (w0[3] | w1[0] | w1[1]) | (w1[2] | w1[3]);
+    if (__builtin_expect(__any((any & 0x40004000u) != 0u), 0)) {
+        const float ma = max3f(sc[0], sc[1], sc[2]);
+        const float mb = max3f(sc[3], sc[4], sc[5]);
+        const float mc = max3f(sc[6], sc[7], sc[8]);
+        const float md = max3f(sc[9], sc[10], sc[11]);
+        const float me = max3f(sc[12], sc[13], sc[14]);
+        const float mx = max3f(max3f(ma, mb, mc), fmaxf(md, me), sc[15]);
+        const float m_new = fmaxf(fmaf(fmaxf(mx, __shfl_xor(mx, 32)), A.c, 7.f), A.M);
+        const float alpha = __builtin_amdgcn_exp2f(A.M - m_new);
         A.M = m_new;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) A.lp[e] *= alpha;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             A.o0[r] *= alpha;
             A.o1[r] *= alpha;
         }
+        // rs[0] of lane n is query n's (alpha of this lane), rs[1] query n+16's
+        A.rs[0] *= alpha;
+        A.rs[1] *= __shfl_down(alpha, 16);
+        weights(sc, A.c, A.M, pn);
     }
-    // LDS operands: V^T fragments of this half, K fragments of the next.
-    bf16x8 v[2][2], k[4];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        v[m][0] = *(const bf16x8*)(vt + foff[2 * kb + m]);
-        v[m][1] = *(const bf16x8*)(vt + kHalfBytes + foff[2 * kb + m]);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) k[j] = *(const bf16x8*)(knext + foff[j]);
-    // p = exp2(t), rounded to bf16 in pairs for the products; the row sums
-    // add the fp32 weights (plain adds: the bf16 dot instruction would hold
-    // up the matrix core).
-    bf16x2 pr[8];
-    const f32x16 zero = {};
-    const float nm = -A.M;
-#define RPKV_EXP_PAIR(e)                                                                           \
-    do {                                                                                           \
-        const f32x2 x_ = {__builtin_amdgcn_exp2f(fmaf(sc[2 * (e)], A.c, nm)),                      \
-                          __builtin_amdgcn_exp2f(fmaf(sc[2 * (e) + 1], A.c, nm))};                 \
-        pr[e] = __builtin_convertvector(x_, bf16x2);                                               \
-        A.lp[(e) & 3] += x_[0] + x_[1];                                                            \
-    } while (0)
-    nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[0], qf[0], zero, 0, 0, 0);
-    RPKV_EXP_PAIR(0);
-    RPKV_EXP_PAIR(1);
-    nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[1], qf[1], nxt, 0, 0, 0);
-    RPKV_EXP_PAIR(2);
-    RPKV_EXP_PAIR(3);
-    const bf16x8 pb0 = __builtin_shufflevector(__builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3),
-                                               __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3),
-                                               0, 1, 2, 3, 4, 5, 6, 7);
-    nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[2], qf[2], nxt, 0, 0, 0);
-    A.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[0][0], pb0, A.o0, 0, 0, 0);
-    RPKV_EXP_PAIR(4);
-    RPKV_EXP_PAIR(5);
-    nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[3], qf[3], nxt, 0, 0, 0);
-    A.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[0][1], pb0, A.o1, 0, 0, 0);
-    RPKV_EXP_PAIR(6);
-    RPKV_EXP_PAIR(7);
-#undef RPKV_EXP_PAIR
-    const bf16x8 pb1 = __builtin_shufflevector(__builtin_shufflevector(pr[4], pr[5], 0, 1, 2, 3),
-                                               __builtin_shufflevector(pr[6], pr[7], 0, 1, 2, 3),
-                                               0, 1, 2, 3, 4, 5, 6, 7);
-    A.o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[1][0], pb1, A.o0, 0, 0, 0);
-    A.o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[1][1], pb1, A.o1, 0, 0, 0);
-    // Keep this half's row sums here (not sunk past the barrier that may
-    // follow), so its weights die now.
-#pragma unroll
-    for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(A.lp[e]));
-    __builtin_amdgcn_sched_barrier(0);
 }
 
-__global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
-    __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attend_bf16(AttnArgs a) {
+    __shared__ __attribute__((aligned(1024))) char ring[2 * kStages * kTileBytes];
     __shared__ int s_vlen[kMaxPool];   // tokens of each visible patch page
-    char* const kring = lds;
-    char* const vring = lds + kKStages * kTileBytes;
+    char* const k0 = ring;
+    char* const k1 = ring + kTileBytes;
+    char* const k2 = ring + 2 * kTileBytes;
+    char* const v0 = ring + 3 * kTileBytes;
+    char* const v1 = ring + 4 * kTileBytes;
+    char* const v2 = ring + 5 * kTileBytes;
 
     // Logical workgroup id: consecutive physical ids go round-robin to the 8
     // XCDs, so the remap gives each XCD a contiguous range of logical ids; the
@@ -245,12 +303,14 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
     const int per_xcd = gridDim.x / 8;
     const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (L >= a.n_logical) return;
-    const int qt = L % a.q_tiles;
-    int rest = L / a.q_tiles;
-    const int split = rest % a.splits;
-    rest /= a.splits;
-    const int h = rest % a.H;
-    const int s = rest / a.H;
+    // (all uniform: kept in scalar registers, so the cache state and the
+    // visible table are read through the scalar cache)
+    const int qt = uniform(L % a.q_tiles);
+    int rest = uniform(L / a.q_tiles);
+    const int split = uniform(rest % a.splits);
+    rest = uniform(rest / a.splits);
+    const int h = uniform(rest % a.H);
+    const int s = uniform(rest / a.H);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     const int hh = lane >> 5, col = lane & 31;
@@ -275,9 +335,7 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
         ld.ksp = buffer_over(ks, sp_bytes);
         ld.vsp = buffer_over(vs, sp_bytes);
     }
-    ld.vis = st->vis;
-    ld.vis_n = vis_n;
-    ld.tpp = a.tpp;
+    ld.vis = (cint_ptr)(uintptr_t)st->vis;
     ld.slot_cap = a.slot_cap;
     // LDS tile layout: row r at r*128 bytes, its 16-byte chunk c stored at
     // position c ^ ((r >> 1) & 7).  A 128-byte row spans half of the 64 LDS
@@ -320,6 +378,17 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
             qf[dc] = __builtin_bit_cast(bf16x8, u);
         }
     }
+    // Selection operand of the row sums (A of v_mfma_f32_16x16x32_bf16, lane
+    // l holds row l%16, k-columns 8*(l/16)..+7): a P^T block used as the B
+    // operand puts the keys of query n in k-groups 0 and 2 and those of query
+    // n+16 in groups 1 and 3 (column n), so row 0 sums query n, row 1 query n+16.
+    bf16x8 sel;
+    {
+        const int m = lane & 15, g = lane >> 4;
+        const __bf16 v = (__bf16)(((m == 0 && (g & 1) == 0) || (m == 1 && (g & 1) == 1)) ? 1.f : 0.f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sel[i] = v;
+    }
 
     Acc A;
 #pragma unroll
@@ -327,11 +396,11 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
         A.o0[i] = 0.f;
         A.o1[i] = 0.f;
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) A.lp[e] = 0.f;
-    A.M = 0.f;
+    A.rs = f32x4{0.f, 0.f, 0.f, 0.f};
+    // A finite start far below any score: the first valid weights come out
+    // infinite, which moves M to their max.
+    A.M = -1e30f;
     A.c = a.scale_log2;
-    A.first = true;
 
     // Operand byte offsets inside a tile ((row >> 1) & 7 == (col >> 1) & 7 for
     // every 32-row block).
@@ -344,74 +413,109 @@ __global__ __launch_bounds__(256) void k_attend_bf16(AttnArgs a) {
     const bool vis_full = uniform(st->vis_full) != 0;
     if (!vis_full)
         for (int i = tid; i < vis_n; i += 256) s_vlen[i] = st->vis_len[i];
-
-    // Prologue: tiles 0 and 1 in flight; wait for tile 0 (the barrier also
-    // publishes s_vlen).
-    if (n > 0) ld.issue(t0, kring, vring, wave);
-    if (n > 1) ld.issue(t0 + 1, kring + kTileBytes, vring + kTileBytes, wave);
-    if (n > 1)
-        wait_vmcnt<4>();
-    else
-        wait_vmcnt<0>();
-    __syncthreads();
-
-    // sA: first half of the tile being computed, sB: its second half.  The
-    // products of a half are formed one half ahead of its softmax; past the
-    // last tile they read a stale stage and are never used.
-    // Valid keys of a tile: a patch page holds the tokens its frame had
-    // (tiles past them have none), the special stream vis_sp.  Worked out
-    // one tile ahead from a walk over (page, tile in page); the page length
-    // is looked up once per page, and not at all when every page is whole.
     auto page_len = [&](int pi) { return vis_full ? a.P : uniform(s_vlen[pi]); };
-    int wpi = t0 / a.tpp, wti = t0 % a.tpp;   // walk position: the next tile
-    int wpl = wpi < vis_n ? page_len(wpi) : 0;
-    auto walk_len = [&](int t) {
-        return t < n_patch_tiles ? min(kTile, wpl - wti * kTile)
-                                 : min(kTile, vis_sp - (t - n_patch_tiles) * kTile);
-    };
-    auto walk_next = [&]() {
-        if (++wti == a.tpp) {
-            wti = 0;
-            ++wpi;
-            if (wpi < vis_n) wpl = page_len(wpi);
+
+    __syncthreads();   // publishes s_vlen
+
+    if (n > 0) {
+        // Two walks: wk issues K tiles three ahead, wv issues V^T tiles two
+        // ahead and gives the valid keys of the tile it is at (a patch page
+        // holds the tokens its frame had, the special stream vis_sp).
+        const int npt = n_patch_tiles, tpp = a.tpp;
+        TileWalk wk, wv;
+        wk.init(t0, npt, tpp, ld.vis);
+        wv = wk;
+        int plen = wv.t < npt ? page_len(wv.pi) : 0;   // tokens of wv's page
+        auto tile_len = [&]() {
+            return wv.t < npt ? min(kTile, plen - wv.tip * kTile) : min(kTile, vis_sp - (wv.t - npt) * kTile);
+        };
+        auto next_v = [&]() {
+            if (wv.next(npt, tpp, ld.vis)) plen = page_len(wv.pi);
+        };
+        // Prologue: K(0..2) and V^T(0..1); the V^T stage the first step's
+        // (empty) products read is zeroed so that stale LDS contents cannot
+        // reach them.
+        ld.issue_k(wk, npt, k0, wave);
+        wk.next(npt, tpp, ld.vis);
+        if (n > 1) {
+            ld.issue_k(wk, npt, k1, wave);
+            wk.next(npt, tpp, ld.vis);
         }
-    };
-    int len_next = walk_len(t0);
-    f32x16 sA = scores(kring, 0, foff, qf);
-    f32x16 sB;
-    // Tiles in groups of kGroup, so every stage offset is a constant that
-    // folds into the LDS instructions' immediate offsets.
-    for (int i0 = 0; i0 < n; i0 += kGroup) {
-#pragma unroll
-        for (int u = 0; u < kGroup; ++u) {
-            const int i = i0 + u, t = t0 + i;
-            if (i >= n) break;
-            const char* kcur = kring + (u % kKStages) * kTileBytes;
-            const char* knxt = kring + ((u + 1) % kKStages) * kTileBytes;
-            const char* vcur = vring + (u % kVStages) * kTileBytes;
-            const int len = len_next;
-            walk_next();
-            len_next = walk_len(t + 1);
-            step(sA, sB, vcur, 0, len, kcur + kHalfBytes, foff, qf, hh, A);
-            if (i + 1 < n) {
-                // Tile i+1 landed for every wave, every wave is done with K of
-                // tile i and V^T of tile i-1: their stages take tile i+2.
-                wait_vmcnt<0>();
-                __syncthreads();
-                if (i + 2 < n)
-                    ld.issue(t + 2, kring + ((u + 2) % kKStages) * kTileBytes,
-                             vring + ((u + 2) % kVStages) * kTileBytes, wave);
+        if (n > 2) {
+            ld.issue_k(wk, npt, k2, wave);
+            wk.next(npt, tpp, ld.vis);
+        }
+        int la = 0, lb = 0, lc = 0;   // valid keys of tiles i, i+1, i+2 (rotating)
+        ld.issue_v(wv, npt, v0, wave);
+        la = tile_len();
+        next_v();
+        if (n > 1) {
+            ld.issue_v(wv, npt, v1, wave);
+            lb = tile_len();
+            next_v();
+        }
+        *(uint4*)(v2 + tid * 16) = make_uint4(0, 0, 0, 0);
+        *(uint4*)(v2 + 4096 + tid * 16) = make_uint4(0, 0, 0, 0);
+        wait_vmcnt<0>();
+        __syncthreads();
+
+        f32x16 sa = scores(k0, 0, foff, qf), sb;
+        bf16x8 pa[2], pb[2];
+        pb[0] = bf16x8{};
+        pb[1] = bf16x8{};
+        // half (0, 0): scores of (0, 1), (empty) products against the zeroed stage
+        step(sa, sb, pa, pb, k0 + kHalfBytes, v2, 1, la < 32, la - 4 * hh, foff, qf, sel, A);
+        __syncthreads();
+        // From the barrier after half (i, 0), with K(i) in kc, K(i+1) in kn,
+        // V^T(i) in vc and V^T(i-1) in vp, and the valid keys of tiles i,
+        // i+1, i+2 in lcur, lnext, lnext2: the stages of K(i) and V^T(i-1)
+        // take K(i+3) and V^T(i+2); half (i, 1); half (i+1, 0); then the
+        // barrier after it, once the loads issued at the previous barrier
+        // (K(i+2), V^T(i+1)) have landed.  Returns false after the last tile.
+        auto tile = [&](int i, char* kc, char* kn, char* vc, char* vp, int& lcur, int& lnext,
+                        int& lnext2) {
+            int issued = 0;   // loads of this wave in flight from this barrier
+            if (i + 3 < n) {
+                ld.issue_k(wk, npt, kc, wave);
+                wk.next(npt, tpp, ld.vis);
+                issued += 2;
             }
-            if (len > 32)
-                step(sB, sA, vcur, 1, len, knxt, foff, qf, hh, A);
+            if (i + 2 < n) {
+                ld.issue_v(wv, npt, vp, wave);
+                lnext2 = tile_len();
+                next_v();
+                issued += 2;
+            }
+            // half (i, 1): scores of (i+1, 0) (past the last tile: a stale
+            // stage, never used), products of (i, 0)
+            step(sb, sa, pb, pa, kn, vc, 0, lcur < 64, lcur - 32 - 4 * hh, foff, qf, sel, A);
+            if (i + 1 == n) return false;
+            // half (i+1, 0): scores of (i+1, 1), products of (i, 1)
+            step(sa, sb, pa, pb, kn + kHalfBytes, vc, 1, lnext < 32, lnext - 4 * hh, foff, qf, sel, A);
+            if (issued == 4)
+                wait_vmcnt<4>();
+            else if (issued == 2)
+                wait_vmcnt<2>();
             else
-                sA = scores(knxt, 0, foff, qf);
+                wait_vmcnt<0>();
+            __syncthreads();
+            return true;
+        };
+        for (int i = 0;; i += 3) {
+            if (!tile(i, k0, k1, v0, v2, la, lb, lc)) break;
+            if (!tile(i + 1, k1, k2, v1, v0, lb, lc, la)) break;
+            if (!tile(i + 2, k2, k0, v2, v1, lc, la, lb)) break;
         }
+        // products of the last half
+        const int last = (n - 1) % 3;
+        products(pb, last == 0 ? v0 : last == 1 ? v1 : v2, 1, foff, sel, A);
     }
 
-    // Row sum over both half-waves; output O = O^T / l.
-    float l = (A.lp[0] + A.lp[1]) + (A.lp[2] + A.lp[3]);
-    l += __shfl_xor(l, 32);
+    // Row sum of the lane's query (rows 0 / 1 of the row-sum block, lanes
+    // 0-15); output O = O^T / l.
+    const float l0 = __shfl(A.rs[0], col & 15);
+    const float l1 = __shfl(A.rs[1], col & 15);
+    const float l = col < 16 ? l0 : l1;
     const bool empty = !(l > 0.f);
     const float inv = empty ? 0.f : 1.f / l;
     const float lse_v = empty ? -INFINITY : (A.M + __log2f(l)) * 0.69314718055994531f;
