@@ -6,6 +6,8 @@ first frames, and at a reduced size through eviction and page recycling.
 
 Bars as in test_gpu_parity: bf16 outputs within 2e-2 max-abs of the float64
 oracle, LSE within 1e-2, page tables bit-exact."""
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -77,6 +79,80 @@ def test_long_stream_1024_frames_keyframe_every_5th():
     st = cache.state()
     assert st["n_special_tokens"] == 1230 and st["free_list"] == [10] and st["fresh"] == 73
     print(f"long stream: max|out-oracle| {worst[0]:.3e}  max|lse-oracle| {worst[1]:.3e}")
+
+
+def test_long_stream_every_frame_on_fixed_rows():
+    """The 1024-frame stream (keyframe every 5th), every frame: the output and
+    LSE of a fixed row sample -- the 6 special tokens and the first and last
+    patch token -- against the float64 oracle, on 2 heads per frame (head
+    h at frames f with f % 8 == h % 8, so every head every 8th frame).
+
+    The retained set of each frame is the oracle's enumeration
+    (OracleStream.visible); the K/V of the retained frames (OracleStream.kv,
+    computed a few frames ahead in threads) sit in a CPU mirror, one slot per retained frame (a frame that leaves the
+    set frees its slot for the next stored one), and the oracle's attention
+    runs on each checked head's keys: stored patches, the frame's own patches,
+    stored specials, its own specials.  Softmax does not depend on the order
+    of the keys, so this is the oracle stream's computation without
+    re-gathering ~1.6 GB of keys per frame."""
+    from oracle import attention as att
+    wl = WORKLOADS[2]
+    cache = make_cache(wl)
+    run = Runner(wl, cache)
+    ost = OracleStream(wl, lambda f, t: qkv(wl, 0, 0, f, t))
+    ns, P, H, D = wl.n_special, wl.patches, wl.heads, wl.head_dim
+    rows = np.r_[np.arange(ns), ns, wl.tokens - 1]
+    n_slots = wl.scale_frames + wl.sliding_window
+    Kp, Vp = np.zeros((H, n_slots * P, D)), np.zeros((H, n_slots * P, D))
+    Ks, Vs = np.zeros((H, wl.n_keyframes() * ns, D)), np.zeros((H, wl.n_keyframes() * ns, D))
+    slot_of, free, n_sp = {}, [], 0
+    last = None   # (frame, K, V) of the previous frame, stored if it was a keyframe
+    worst = [0.0, 0.0]
+
+    def oracle_frame(f):
+        # the oracle's rotated K, V and Q rows of frame f (independent of the
+        # mirror: computed ahead, several frames at a time)
+        o = OracleStream(wl, lambda f_, t: qkv(wl, 0, 0, f_, t))
+        kf, vf = o.kv(f)
+        return kf, vf, o.q_rot(f)[rows]
+
+    pool = ThreadPoolExecutor(8)
+    ahead = {}
+    for f, q, k, v in stream_frames(wl, None):
+        if f not in ahead:
+            ahead = {g: pool.submit(oracle_frame, g) for g in range(f, min(wl.frames, f + 32))}
+        kf, vf, qr = ahead.pop(f).result()
+        run.frame(f, q, k, v, wl.is_keyframe(f))
+        pf, sf = ost.visible(f)
+        stored_p, stored_s = [g for g in pf if g != f], [g for g in sf if g != f]
+        for g in [g for g in slot_of if g not in stored_p]:
+            free.append(slot_of.pop(g))
+        if last is not None and last[0] in stored_s:       # the previous frame was stored
+            g, kg, vg = last
+            if g in stored_p:
+                slot = free.pop() if free else len(slot_of)
+                slot_of[g] = slot
+                Kp[:, slot * P:(slot + 1) * P] = kg[ns:].transpose(1, 0, 2)
+                Vp[:, slot * P:(slot + 1) * P] = vg[ns:].transpose(1, 0, 2)
+            Ks[:, n_sp:n_sp + ns] = kg[:ns].transpose(1, 0, 2)
+            Vs[:, n_sp:n_sp + ns] = vg[:ns].transpose(1, 0, 2)
+            n_sp += ns
+        assert sorted(slot_of) == sorted(stored_p) and n_sp == ns * len(stored_s), f
+        last = (f, kf, vf)
+        n_used = len(slot_of)
+        assert sorted(slot_of.values()) == list(range(n_used)), f   # the slots in use are a prefix
+        torch.cuda.synchronize()
+        got = run.out[0].float().cpu().numpy()[rows]
+        got_lse = run.lse[0].cpu().numpy()[:, rows]
+        for h in range(f % 8, H, 8):
+            kk = np.concatenate([Kp[h][:n_used * P], kf[ns:, h], Ks[h][:n_sp], kf[:ns, h]])
+            vv = np.concatenate([Vp[h][:n_used * P], vf[ns:, h], Vs[h][:n_sp], vf[:ns, h]])
+            o, lse = att.attention(qr[:, h], kk, vv)
+            e, le = np.abs(got[:, h] - o).max(), np.abs(got_lse[h] - lse).max()
+            worst = [max(worst[0], e), max(worst[1], le)]
+            assert e <= BF16_TOL and le <= LSE_TOL, (f, h, e, le)
+    pool.shutdown()
+    print(f"long stream, every frame: max|out-oracle| {worst[0]:.3e}  max|lse-oracle| {worst[1]:.3e}")
 
 
 def test_large_grid_64x64():

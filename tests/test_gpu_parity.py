@@ -350,6 +350,15 @@ def test_single_layer_37x37_sampled():
     print(f"37x37 single layer: max|out-oracle| {worst:.3e}  max|lse-oracle| {worst_lse:.3e}")
 
 
+def test_single_layer_37x37_all_rows_at_transitions():
+    """The 37x37 stream in full on three frames: every query row of every head
+    at the first eviction (frame 24), the first recycled page (frame 25) and
+    the last frame (63), against the float64 oracle."""
+    wl = WORKLOADS[1]
+    worst, worst_lse = run_and_compare(wl, {24, 25, 63})
+    print(f"37x37 all rows at frames 24, 25, 63: max|out-oracle| {worst:.3e}  max|lse-oracle| {worst_lse:.3e}")
+
+
 def test_variable_patch_grids():
     """Frames of their own grids (9x11, 7x11, 5x6, 1x1, 9x7 in a 9x11 page):
     pages record their token counts, q_rot and K follow each frame's grid,
