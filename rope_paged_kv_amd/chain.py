@@ -26,7 +26,7 @@ class FullDepthStream:
                  scale_frames: int, sliding_window: int, keyframe_interval: int, frames: int,
                  weights: List[torch.Tensor], head_dim: int = 64, special_tokens: int = 6,
                  pairs=(12, 10, 10), theta: float = 10000.0, ntk_factor: float = 1.0,
-                 attn_splits: int = 0, device="cuda"):
+                 attn_splits: int = 0, frame_splits: int = 1, device="cuda"):
         if layers % 2:
             raise ValueError("layers alternate frame/global: an even count is expected")
         self.S, self.L, self.H, self.D = streams, layers, heads, head_dim
@@ -41,7 +41,8 @@ class FullDepthStream:
         # Frame layers keep nothing: every append is a skip-append on a cache
         # with no scale pages and no window, so one handle serves all of them.
         self.frame_cache = PagedKVCache(make_config(num_layers=1, scale_frames=0, sliding_window=0,
-                                                    max_keyframes=0, attn_splits=1, **common),
+                                                    max_keyframes=0, attn_splits=frame_splits,
+                                                    **common),
                                         device=self.device)
         n_kf = (frames + keyframe_interval - 1) // keyframe_interval
         self.global_cache = PagedKVCache(make_config(num_layers=layers // 2,
@@ -90,5 +91,5 @@ class FullDepthStream:
                 c.evict(g)
             if keep is not None:
                 keep.append(self.out.clone())
-            x.add_(self.out.view(self.S, self.N, self.hidden).float())
+            x.add_(self.out.view(self.S, self.N, self.hidden))   # bf16 added into fp32, one kernel
         return x

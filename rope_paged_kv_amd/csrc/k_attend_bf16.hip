@@ -188,16 +188,18 @@ struct Acc {
     float c;           // log2(e)/sqrt(D)
 };
 
-// s = q.k for the 32 keys of half kb of a tile (rows 32*kb + col of the K
-// tile; chunk 2*j + hh is k-step j).
-__device__ __forceinline__ f32x16 scores(const char* tile, int kb, const int* foff, const bf16x8* qf) {
+// s = q.k + init for the 32 keys of half kb of a tile (rows 32*kb + col of
+// the K tile; chunk 2*j + hh is k-step j).  init is the accumulator's start:
+// 0 for a key that counts, -inf for one past the end of a ragged half, so the
+// mask costs nothing in the steps.
+__device__ __forceinline__ f32x16 scores(const char* tile, int kb, const int* foff, const bf16x8* qf,
+                                         const f32x16& init) {
     const char* t = tile + kb * kHalfBytes;
     const bf16x8 k0 = *(const bf16x8*)(t + foff[0]);
     const bf16x8 k1 = *(const bf16x8*)(t + foff[1]);
     const bf16x8 k2 = *(const bf16x8*)(t + foff[2]);
     const bf16x8 k3 = *(const bf16x8*)(t + foff[3]);
-    const f32x16 zero = {};
-    f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[0], zero, 0, 0, 0);
+    f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[0], init, 0, 0, 0);
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[1], s, 0, 0, 0);
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k2, qf[2], s, 0, 0, 0);
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k3, qf[3], s, 0, 0, 0);
@@ -240,19 +242,15 @@ __device__ __forceinline__ void weights(const f32x16& sc, float c, float M, bf16
 }
 
 // One pipeline step: the softmax weights pn of the half whose scores are sc
-// (rag: a ragged half, whose keys at or past lim -- its valid count minus
-// 4*hh -- do not count), the scores sn of the next half (K rows at knext) and
-// the output products of the previous half (weights pp, V^T half vkb of the
-// tile at vprev).  Key of sc[r]: 8*(r/4) + 4*hh + r%4 within the half.
+// (keys past a ragged half's end already at -inf), the scores sn of the next
+// half (K rows at knext, accumulator started at init) and the output products
+// of the previous half (weights pp, V^T half vkb of the tile at vprev).  Key of
+// sc[r]: 8*(r/4) + 4*hh + r%4 within the half.  No branch but the rare
+// rescale, so the operand reads of the step overlap its products.
 __device__ __forceinline__ void step(f32x16& sc, f32x16& sn, bf16x8 (&pn)[2], const bf16x8 (&pp)[2],
-                                     const char* knext, const char* vprev, int vkb, bool rag, int lim,
+                                     const char* knext, const char* vprev, int vkb, const f32x16& init,
                                      const int* foff, const bf16x8* qf, const bf16x8& sel, Acc& A) {
-    if (rag) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if (8 * (r >> 2) + (r & 3) >= lim) sc[r] = -INFINITY;
-    }
-    sn = scores(knext, 0, foff, qf);
+    sn = scores(knext, 0, foff, qf, init);
     products(pp, vprev, vkb, foff, sel, A);
     weights(sc, A.c, A.M, pn);
     // M is kept 7 above the largest exponent seen when it last moved, so the
@@ -459,12 +457,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         wait_vmcnt<0>();
         __syncthreads();
 
-        f32x16 sa = scores(k0, 0, foff, qf), sb;
+        // Accumulator start of the next score products: zero, or -inf on the
+        // keys past the end of a ragged half (set only when one comes).
+        f32x16 init = {};
+        bool masked = false;
+        auto set_init = [&](int len, int kb) {   // for half kb of a tile of len valid keys
+            const int lim = len - 32 * kb - 4 * hh;
+            if (len >= 32 * kb + 32) {
+                if (masked) {
+                    init = f32x16{};
+                    masked = false;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) init[r] = 8 * (r >> 2) + (r & 3) >= lim ? -INFINITY : 0.f;
+                masked = true;
+            }
+        };
+        set_init(la, 0);
+        f32x16 sa = scores(k0, 0, foff, qf, init), sb;
         bf16x8 pa[2], pb[2];
         pb[0] = bf16x8{};
         pb[1] = bf16x8{};
         // half (0, 0): scores of (0, 1), (empty) products against the zeroed stage
-        step(sa, sb, pa, pb, k0 + kHalfBytes, v2, 1, la < 32, la - 4 * hh, foff, qf, sel, A);
+        set_init(la, 1);
+        step(sa, sb, pa, pb, k0 + kHalfBytes, v2, 1, init, foff, qf, sel, A);
         __syncthreads();
         // From the barrier after half (i, 0), with K(i) in kc, K(i+1) in kn,
         // V^T(i) in vc and V^T(i-1) in vp, and the valid keys of tiles i,
@@ -488,10 +505,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             }
             // half (i, 1): scores of (i+1, 0) (past the last tile: a stale
             // stage, never used), products of (i, 0)
-            step(sb, sa, pb, pa, kn, vc, 0, lcur < 64, lcur - 32 - 4 * hh, foff, qf, sel, A);
+            set_init(lnext, 0);
+            step(sb, sa, pb, pa, kn, vc, 0, init, foff, qf, sel, A);
             if (i + 1 == n) return false;
             // half (i+1, 0): scores of (i+1, 1), products of (i, 1)
-            step(sa, sb, pa, pb, kn + kHalfBytes, vc, 1, lnext < 32, lnext - 4 * hh, foff, qf, sel, A);
+            set_init(lnext, 1);
+            step(sa, sb, pa, pb, kn + kHalfBytes, vc, 1, init, foff, qf, sel, A);
             if (issued == 4)
                 wait_vmcnt<4>();
             else if (issued == 2)
