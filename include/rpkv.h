@@ -294,6 +294,22 @@ int attend_frame(kv_handle* h, int layer, const void* q_rot, void* out, float* l
 int attend_frame_noalloc(kv_handle* h, int layer, const void* q_rot, void* out, float* lse,
                          void* stream);
 
+/*
+ * Residual update after an attention layer, fused with the cast feeding the
+ * next layer's projection (page "How LingBot-Map Achieves Real-Time 3D
+ * Reconstruction", section "AggregatorStream with FlashInfer Paged KV Cache":
+ * each frame and global block adds its attention output back into the token
+ * stream).  For i in [0, n):
+ *   x[i]  <- x[i] + o[i]       in fp32 (o widened exactly, one rounding)
+ *   xb[i] <- x[i] rounded to bf16, nearest even (NaN stays NaN)
+ *   x:  fp32, read and written;  o: bf16 bits, read only (attend_frame's out
+ *       viewed flat);  xb: bf16 bits, written, or NULL to skip the cast.
+ * Elementwise, so any shape flattened to n elements; x, o and xb must not
+ * overlap.  n = 0 launches nothing.  EINVAL for n < 0 or n >= 2^40, or a
+ * pointer that is null (xb aside) or not 16-byte aligned.
+ */
+int residual_add_bf16(float* x, const void* o, void* xb, long long n, void* stream);
+
 /* Deferred eviction for `layer` ([KVB] "Memory-Efficient Sliding Window
  * Management", "Dynamic Keyframe Selection"; [ROPE-KV] "Dual-Stream Memory
  * Layout"), run after the frame's attention: first keeps the last appended

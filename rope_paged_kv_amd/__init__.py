@@ -124,6 +124,24 @@ def attend_frame_noalloc(h, layer: int, q_rot, out, lse, stream: int) -> None:
            "attend_frame_noalloc")
 
 
+def residual_add_bf16(x, o, xb, n: int, stream: int) -> None:
+    _check(_lib.residual_add_bf16(_vp(x), _vp(o), _vp(xb), n, stream), "residual_add_bf16")
+
+
+def residual_add(x, o, xb=None) -> None:
+    """x += o (fp32 += bf16) and, if given, xb = bf16(x), on torch's current
+    stream: x fp32, o and xb bf16, contiguous, on one device, o and xb with
+    x's number of elements."""
+    import torch
+    if x.dtype != torch.float32 or o.dtype != torch.bfloat16 or not x.is_contiguous() \
+            or not o.is_contiguous() or o.numel() != x.numel() or o.device != x.device:
+        raise ValueError("residual_add: x fp32 and o bf16, contiguous, same size and device")
+    if xb is not None and (xb.dtype != torch.bfloat16 or not xb.is_contiguous()
+                           or xb.numel() != x.numel() or xb.device != x.device):
+        raise ValueError("residual_add: xb bf16, contiguous, x's size and device")
+    residual_add_bf16(x, o, xb, x.numel(), torch.cuda.current_stream(x.device).cuda_stream)
+
+
 def kv_evict_deferred(h, layer: int, stream: int) -> None:
     _check(_lib.kv_evict_deferred(h, layer, stream), "kv_evict_deferred")
 

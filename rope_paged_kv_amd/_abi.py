@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librpkv.so"
 
 EXPORTS = ("rope3d_tables_bytes", "rope3d_build_tables", "kv_required_bytes", "kv_create",
            "kv_destroy", "kv_reset", "kv_append_frame", "kv_append_frame_grid", "kv_project_append_frame", "kv_project_append_frame_grid", "attend_frame",
-           "attend_frame_noalloc", "kv_evict_deferred",
+           "attend_frame_noalloc", "residual_add_bf16", "kv_evict_deferred",
            "kv_rollback", "kv_read_state", "kv_get_info", "rpkv_strerror")
 
 
@@ -83,6 +83,7 @@ def load() -> C.CDLL:
         "kv_project_append_frame_grid": (i, [vp, i, i, i, i, i, vp, i, vp, vp, vp, vp]),
         "attend_frame": (i, [vp, i, vp, vp, vp, vp]),
         "attend_frame_noalloc": (i, [vp, i, vp, vp, vp, vp]),
+        "residual_add_bf16": (i, [vp, vp, vp, C.c_longlong, vp]),
         "kv_evict_deferred": (i, [vp, i, vp]),
         "kv_rollback": (i, [vp, i, vp]),
         "kv_read_state": (i, [vp, i, i, C.POINTER(KvStateHost), vp]),

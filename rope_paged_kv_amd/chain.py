@@ -6,9 +6,10 @@ streams batched in every call.
 Per layer: the library's fused projection + RoPE + append
 (kv_project_append_frame: [Q | K | V] = bf16(x) W_l^T on the matrix cores,
 rotated and written straight to q_rot and the pages), attention and (global
-layers) deferred eviction, then the residual x <- x + O in fp32.  Frame and
-global blocks are named on page "How LingBot-Map Achieves Real-Time 3D
-Reconstruction", section "AggregatorStream with FlashInfer Paged KV Cache";
+layers) deferred eviction, then the residual x <- x + O in fp32, fused with
+the cast to bf16 that feeds the next layer's projection (residual_add_bf16).
+Frame and global blocks are named on page "How LingBot-Map Achieves Real-Time
+3D Reconstruction", section "AggregatorStream with FlashInfer Paged KV Cache";
 the block internals need trained weights, so this driver keeps only the
 projection, the attention and the residual.
 """
@@ -18,7 +19,7 @@ from typing import List, Optional
 
 import torch
 
-from . import PagedKVCache, make_config, make_spec
+from . import PagedKVCache, make_config, make_spec, residual_add
 
 
 class FullDepthStream:
@@ -70,8 +71,8 @@ class FullDepthStream:
         `events` (around each fused projection + append to `proj_events`) if
         given."""
         commit = int(f % self.interval == 0)
+        self.xb.copy_(x)   # later layers get their bf16 input from the residual kernel
         for layer in range(self.L):
-            self.xb.copy_(x)
             c, g, cm = (self.frame_cache, 0, 0) if layer % 2 == 0 else (self.global_cache, layer // 2, commit)
             if proj_events is not None:
                 p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -91,5 +92,6 @@ class FullDepthStream:
                 c.evict(g)
             if keep is not None:
                 keep.append(self.out.clone())
-            x.add_(self.out.view(self.S, self.N, self.hidden))   # bf16 added into fp32, one kernel
+            # x += O in fp32 and the next layer's bf16 input, in one pass
+            residual_add(x, self.out, self.xb if layer + 1 < self.L else None)
         return x

@@ -429,6 +429,13 @@ int attend_frame_noalloc(kv_handle* h, int layer, const void* q_rot, void* out, 
     return hip_status(launch_attend(a, h->cfg.dtype, (hipStream_t)stream));
 }
 
+int residual_add_bf16(float* x, const void* o, void* xb, long long n, void* stream) {
+    if (n < 0 || n >= (1LL << 40) || !x || !o) return RPKV_EINVAL;
+    if (!aligned16(x) || !aligned16(o) || (xb && !aligned16(xb))) return RPKV_EINVAL;
+    if (n == 0) return RPKV_OK;
+    return hip_status(launch_residual_add(x, (const uint16_t*)o, (uint16_t*)xb, n, (hipStream_t)stream));
+}
+
 int kv_evict_deferred(kv_handle* h, int layer, void* stream) {
     if (!h || layer < 0 || layer >= h->cfg.num_layers) return RPKV_EINVAL;
     const Layout& L = h->L;

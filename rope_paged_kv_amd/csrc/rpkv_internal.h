@@ -123,5 +123,7 @@ hipError_t launch_rope_append(const AppendArgs& a, int dtype, hipStream_t st);
 hipError_t launch_project_append(const ProjArgs& p, hipStream_t st);
 hipError_t launch_attend(const AttnArgs& a, int dtype, hipStream_t st);
 hipError_t launch_attend_bf16_main(const AttnArgs& a, hipStream_t st);
+hipError_t launch_residual_add(float* x, const uint16_t* o, uint16_t* xb, long long n,
+                               hipStream_t st);
 
 }  // namespace rpkv

@@ -80,3 +80,14 @@ def test_vslot_perm_is_an_involution_on_16_groups():
         assert vslot_perm(vslot_perm(p)) == p
         assert vslot_perm(p) // 16 == p // 16
     assert [vslot_perm(p) for p in range(16)] == [0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15]
+
+
+def test_residual_add_validates_before_launching():
+    import rope_paged_kv_amd as r
+    for x, o, xb, n in ((256, 512, 768, -1), (0, 512, 768, 8), (256, 0, 768, 8),
+                        (264, 512, 768, 8), (256, 520, 768, 8), (256, 512, 776, 8),
+                        (256, 512, None, 1 << 40)):
+        with pytest.raises(r.RpkvError) as e:
+            r.residual_add_bf16(x, o, xb, n, 0)
+        assert e.value.code == r.RPKV_EINVAL, (x, o, xb, n)
+    r.residual_add_bf16(256, 512, None, 0, 0)   # n = 0 launches nothing

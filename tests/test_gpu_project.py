@@ -201,3 +201,30 @@ def test_project_append_variable_grids():
             assert np.abs(lse[s, :, :n].cpu().numpy() - lse_want).max() <= LSE_TOL, (f, s)
         sim.evict()
         cache.evict(0)
+
+
+@pytest.mark.parametrize("n", [5, 8 * 37 + 3, 4 * 1375 * 1024])
+def test_residual_add_is_the_fp32_sum_and_its_bf16_rounding(n):
+    """residual_add_bf16 against its definition on the CPU: x + o in fp32,
+    then round to nearest even into bf16 -- bit for bit, at a length below
+    one 8-element chunk, one with a ragged tail, and the full-depth
+    workload's [4][1375][1024].  Values span bf16 rounding ties and sums that
+    overflow to inf."""
+    g = torch.Generator().manual_seed(n)
+    x = torch.randn(n, generator=g) * 3
+    o = (torch.randn(n, generator=g) * 3).to(torch.bfloat16)
+    x[:2] = torch.tensor([3.0e38, 1.0 + 2.0 ** -8])         # overflow; a tie of bf16 rounding
+    o[:2] = torch.tensor([3.0e38, 0.0]).to(torch.bfloat16)
+    want_x = x + o.float()
+    want_xb = want_x.to(torch.bfloat16)
+    xd, od = x.cuda(), o.cuda()
+    xbd = torch.full((n,), 7.0, dtype=torch.bfloat16, device="cuda")
+    rp.residual_add(xd, od, xbd)
+    torch.cuda.synchronize()
+    assert torch.equal(xd.cpu().view(torch.int32), want_x.view(torch.int32))
+    assert torch.equal(xbd.cpu().view(torch.int16), want_xb.view(torch.int16))
+    # without the cast: x only, nothing else written
+    xd2 = x.cuda()
+    rp.residual_add(xd2, od, None)
+    torch.cuda.synchronize()
+    assert torch.equal(xd2.cpu().view(torch.int32), want_x.view(torch.int32))
