@@ -149,7 +149,7 @@ def cpu_baseline_chain(wl, frames=3):
             **cpu_host()}
 
 
-def result_line(wl, args, elapsed, frames_per_step, att_ms, att_flops, app_ms, info_splits,
+def result_line(wl, args, elapsed, frames_per_step, att_ms, att_flops, info_splits,
                 unit="frames/s", extra=None, config_extra=None):
     import numpy as np
     att_avg_s = float(np.mean(att_ms)) / 1e3
@@ -182,12 +182,6 @@ def result_line(wl, args, elapsed, frames_per_step, att_ms, att_flops, app_ms, i
                      "algorithmic_flops_per_launch": float(np.mean(att_flops))},
         "extra": extra or {},
     }
-    if app_ms is not None:
-        app_gbs = append_bytes(wl) / (float(np.mean(app_ms)) / 1e3) / 1e9
-        res["extra"].update({"rope_append_gbs": round(app_gbs, 1),
-                             "rope_append_hbm_frac": round(app_gbs / HBM_PEAK_GBS, 4),
-                             "rope_append_avg_us": round(float(np.mean(app_ms)) * 1e3, 2),
-                             "rope_append_bytes_per_launch": append_bytes(wl)})
     return res
 
 
@@ -221,19 +215,17 @@ def bench_single_layer(wl, args, dev):
     def one_pass(ev=None):
         cache.reset(0)
         for f in range(F):
-            if ev is not None:
-                ev[f][0].record()
             cache.append(0, f, keyf[f], q_all[f], k_all[f], v_all[f], q_rot)
             if ev is not None:
-                ev[f][1].record()
+                ev[f][0].record()
             cache.attend(0, q_rot, out, lse)
             if ev is not None:
-                ev[f][2].record()
+                ev[f][1].record()
             cache.evict(0)
 
     for _ in range(args.warmup):
         one_pass()
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(F)]
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(F)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -242,8 +234,7 @@ def bench_single_layer(wl, args, dev):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    att_ms = np.array([[e[f][1].elapsed_time(e[f][2]) for f in range(F)] for e in events])
-    app_ms = np.array([[e[f][0].elapsed_time(e[f][1]) for f in range(F)] for e in events])
+    att_ms = np.array([[e[f][0].elapsed_time(e[f][1]) for f in range(F)] for e in events])
     flops = np.array([attn_flops(wl, f) for f in range(F)])
     steady = [f for f in range(F) if f >= wl.scale_frames + wl.sliding_window]
     extra = {}
@@ -251,7 +242,7 @@ def bench_single_layer(wl, args, dev):
         extra["attend_tflops_steady"] = round(
             float(flops[steady].mean() / (att_ms[:, steady].mean() / 1e3) / 1e12), 2)
     res = result_line(wl, args, elapsed, F * wl.streams, att_ms, np.tile(flops, (args.steps, 1)),
-                      app_ms, cache.info()["attn_splits"], extra=extra)
+                      cache.info()["attn_splits"], extra=extra)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         res["cpu_baseline"] = cpu_baseline(wl)
@@ -312,7 +303,7 @@ def bench_full_depth(wl, args, dev):
     extra.update({"project_append_avg_us": round(proj_us, 2),
                   "project_append_tflops": round(proj_flops / proj_us / 1e6, 1),
                   "project_append_mfma_frac": round(proj_flops / proj_us / 1e6 / BF16_PEAK_TFLOPS, 4)})
-    res = result_line(wl, args, elapsed, F * wl.streams, att_ms, flops, None,
+    res = result_line(wl, args, elapsed, F * wl.streams, att_ms, flops,
                       fds.global_cache.info()["attn_splits"], unit="stream-frames/s", extra=extra,
                       config_extra={"layers": wl.chain_layers, "hidden": wl.hidden,
                                     "includes": "fused QKV projection + RoPE + append, residual"})
@@ -322,10 +313,49 @@ def bench_full_depth(wl, args, dev):
     return res
 
 
+def _spin_cycles_per_ms(dev):
+    """Rate of torch.cuda._sleep (a bounded spin kernel) on this GPU."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    e0.record()
+    torch.cuda._sleep(20_000_000)
+    e1.record()
+    torch.cuda.synchronize()
+    return 20_000_000 / e0.elapsed_time(e1)
+
+
+def _batch_us(fn, count, spin_cycles):
+    """Mean GPU time (us) per call of `count` back-to-back calls fn(i), from one
+    pair of HIP events around the batch.  A spin queued first keeps the GPU
+    busy while the host enqueues the batch, so the kernels run back to back
+    and neither host launch gaps nor per-event overhead enter the figure."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(spin_cycles)
+    e0.record()
+    for i in range(count):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / count
+
+
 def bench_append(wl, args, dev):
     """kv_append_frame alone at the workload's geometry (all streams in one
-    launch): GB/s of its algorithmic bytes, from HIP events around each call."""
-    import numpy as np
+    launch), with a plain device copy of the same bytes (half read, half
+    written) beside it as the achievable rate at this size.
+
+    The cache is first run through the stream's opening frames, then the
+    timed calls append one steady-state frame over and over (each call
+    replaces the previous call's tentative slot, as the C API defines), back
+    to back.  Two input regimes: cold (16 frames of inputs in rotation, more
+    than the caches hold at four streams) and warm (one frame's inputs, read
+    by the previous call: what a producer that has just written q, k, v
+    gives)."""
+    import time
+
     import torch
 
     import rope_paged_kv_amd as rp
@@ -343,39 +373,58 @@ def bench_append(wl, args, dev):
                          max_keyframes=wl.n_keyframes(), rope=spec)
     cache = rp.PagedKVCache(cfg, device=dev)
     q_rot = torch.empty_like(qkv[0][0])
-    F = wl.frames
+    nbytes = append_bytes(wl)
+    src = [torch.cat([t.reshape(-1) for t in f]) for f in qkv]   # the same bytes as q, k, v
+    dst = torch.empty_like(src[0])
+    assert 2 * src[0].numel() * src[0].element_size() == nbytes
 
-    def one_pass(ev=None):
-        cache.reset(0)
-        for f in range(F):
-            q, k, v = qkv[f % nf]
-            if ev is not None:
-                ev[f][0].record()
-            cache.append(0, f, int(wl.is_keyframe(f)), q, k, v, q_rot)
-            if ev is not None:
-                ev[f][1].record()
-            cache.evict(0)
+    # steady state: scale pages and a full window behind the timed frame
+    f_pos = min(wl.frames - 1, wl.scale_frames * wl.keyframe_interval + wl.sliding_window + 2)
+    cache.reset(0)
+    for f in range(f_pos):
+        q, k, v = qkv[f % nf]
+        cache.append(0, f, int(wl.is_keyframe(f)), q, k, v, q_rot)
+        cache.evict(0)
+    commit = int(wl.is_keyframe(f_pos))
 
-    for _ in range(args.warmup):
-        one_pass()
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(F)]
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        one_pass(events[k])
-    torch.cuda.synchronize()
-    us = float(np.mean([[e[f][0].elapsed_time(e[f][1]) for f in range(F)] for e in events])) * 1e3
-    gbs = append_bytes(wl) / us / 1e3
+    def append_fn(rot):
+        return lambda i: cache.append(0, f_pos, commit, *qkv[i % nf if rot else 0], q_rot)
+
+    def copy_fn(rot):
+        return lambda i: dst.copy_(src[i % nf if rot else 0])
+
+    count = wl.frames * args.steps
+    rate = _spin_cycles_per_ms(dev)
+    # host enqueue time of one batch (GPU left to drain), to size the spin
+    t0 = time.perf_counter()
+    for _ in range(max(args.warmup, 1)):
+        _batch_us(append_fn(True), count, 1000)
+    host_ms = (time.perf_counter() - t0) * 1e3 / max(args.warmup, 1)
+    spin = int(rate * (1.5 * host_ms + 2.0))
+    res = {}
+    for name, fn in (("append_cold", append_fn(True)), ("append_warm", append_fn(False)),
+                     ("copy_cold", copy_fn(True)), ("copy_warm", copy_fn(False))):
+        _batch_us(fn, nf, 1000)                         # warm-up
+        us = _batch_us(fn, count, spin)
+        res[name] = (us, nbytes / us / 1e3)
+    cache.rollback(0)
+    us, gbs = res["append_cold"]
+    extra = {k: {"avg_us": round(v[0], 2), "gbs": round(v[1], 1),
+                 "hbm_frac": round(v[1] / HBM_PEAK_GBS, 4)} for k, v in res.items()}
+    extra.update({"cold_frac_of_copy": round(res["copy_cold"][0] / res["append_cold"][0], 3),
+                  "warm_frac_of_copy": round(res["copy_warm"][0] / res["append_warm"][0], 3),
+                  "copy": "device-to-device copy of the same byte count (torch copy_)",
+                  "launches_per_regime": count, "host_enqueue_ms_per_batch": round(host_ms, 2)})
     return {"metric": "kv_append_frame GB/s (RoPE + page write, % HBM)", "value": round(gbs, 1),
             "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "dtype": wl.dtype, "data": "synthetic",
             "config": {"workload": wl.name, "streams": wl.streams,
                        "grid": f"{wl.grid_h}x{wl.grid_w}", "heads": wl.heads,
-                       "frames_per_step": F},
+                       "launches_per_step": wl.frames, "inputs": "cold (16 frames in rotation)"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                         "avg_launch_us": round(us, 2),
-                         "algorithmic_bytes_per_launch": append_bytes(wl)}}
+                         "avg_launch_us": round(us, 2), "algorithmic_bytes_per_launch": nbytes},
+            "extra": extra}
 
 
 def main():
