@@ -17,9 +17,10 @@
 //    appended in order and never evicted, is contiguous per head), each tile
 //    in two halves of 32 keys;
 //  * tiles stream from HBM straight into LDS (buffer_load ... lds: no staging
-//    registers, the page offset in a scalar register) through rings of 2 K
-//    and 2 V^T stages, one barrier per tile; 16-byte chunks are XOR-swizzled
-//    so operand reads hit 64 distinct banks;
+//    registers, the page offset in a scalar register) through rings of 3 K
+//    and 3 V^T stages, each load issued two tiles before its use and waited
+//    for with a counted wait, one barrier per tile; 16-byte chunks are
+//    XOR-swizzled so operand reads hit 64 distinct banks;
 //  * scores are formed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16:
 //    keys on the rows, queries on the columns): each lane holds 16 scores of
 //    one query per half tile; P^T rounded to bf16 is directly the B operand of
