@@ -3,9 +3,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline]
     python bench.py --append-only [--workload W]
 
-One step is one pass of the whole path over one synthetic stream: reset the
-caches, then for every frame RoPE + append, paged attention (attend_frame)
-and deferred eviction (kv_evict_deferred).  The default workload (4) is the
+One step of a single-layer workload is one pass of the whole path over one
+synthetic stream: reset the caches, then for every frame RoPE + append, paged
+attention (attend_frame) and deferred eviction (kv_evict_deferred).  One step
+of the full-depth workload is a quarter of its stream (64 frames through all
+layers; the stream runs on across steps).  The default workload (4) is the
 full-depth stack, the largest single-GPU workload of 37x37-patch frames: 4
 streams of 256 frames (37x37 patches + 6 special tokens, 16 heads of 64,
 bf16), 24 layers alternating frame attention (the frame's own tokens) and
@@ -22,7 +24,8 @@ around every attend_frame launch in the timed region; cpu_baseline = the CPU
 oracle on a bounded sample of the same stream.
 
 --append-only times kv_append_frame alone (RoPE + page write, HBM bound) at
-the workload's geometry, all its streams in one launch, and prints its GB/s.
+the workload's geometry, all its streams in one launch, cold and warm, beside
+a device copy of the same bytes, and prints its GB/s.
 """
 from __future__ import annotations
 
@@ -269,21 +272,30 @@ def bench_full_depth(wl, args, dev):
                           sliding_window=wl.sliding_window, keyframe_interval=wl.keyframe_interval,
                           frames=wl.frames, weights=weights, attn_splits=args.splits, device=dev)
     F = wl.frames
+    # A step is a quarter of the stream: 64 consecutive frames of all streams
+    # through every layer.  The stream runs on across steps and starts again
+    # on an emptied cache at frame 0, so 4 steps are one whole pass (warm-up
+    # included: 5 warm-up and 20 timed steps time every frame exactly 5 times).
+    per_step = min(F, 64)
     x = torch.empty_like(x0[0])
+    cursor = [0]
 
-    def one_pass(ev=None, pev=None):
-        fds.reset()
-        for f in range(F):
+    def one_step(ev=None, pev=None):
+        for _ in range(per_step):
+            f = cursor[0]
+            if f == 0:
+                fds.reset()
             x.copy_(x0[f])
             fds.frame(f, x, events=ev, proj_events=pev)
+            cursor[0] = (f + 1) % F
 
     for _ in range(args.warmup):
-        one_pass()
+        one_step()
     torch.cuda.synchronize()
     evs, pevs = [], []
     t0 = time.perf_counter()
     for k in range(args.steps):
-        one_pass(evs, pevs)
+        one_step(evs, pevs)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     att_ms, flops = [], []
@@ -297,15 +309,19 @@ def bench_full_depth(wl, args, dev):
     glob = np.array([layer % 2 == 1 for (_, layer, _, _) in evs])
     extra = {"attend_tflops_global_layers": round(float(flops[glob].mean() / (att_ms[glob].mean() / 1e3) / 1e12), 2),
              "attend_tflops_frame_layers": round(float(flops[~glob].mean() / (att_ms[~glob].mean() / 1e3) / 1e12), 2),
-             "frame_steps_per_s": round(F * args.steps / elapsed, 3)}
+             "frame_steps_per_s": round(per_step * args.steps / elapsed, 3)}
     proj_us = float(np.mean([e0.elapsed_time(e1) for (_, _, e0, e1) in pevs])) * 1e3
     proj_flops = 2.0 * wl.streams * wl.tokens * wl.hidden * 3 * wl.heads * wl.head_dim
     extra.update({"project_append_avg_us": round(proj_us, 2),
                   "project_append_tflops": round(proj_flops / proj_us / 1e6, 1),
                   "project_append_mfma_frac": round(proj_flops / proj_us / 1e6 / BF16_PEAK_TFLOPS, 4)})
-    res = result_line(wl, args, elapsed, F * wl.streams, att_ms, flops,
+    res = result_line(wl, args, elapsed, per_step * wl.streams, att_ms, flops,
                       fds.global_cache.info()["attn_splits"], unit="stream-frames/s", extra=extra,
                       config_extra={"layers": wl.chain_layers, "hidden": wl.hidden,
+                                    "stream_frames": F,
+                                    "step": f"{per_step} consecutive frames of the {F}-frame streams "
+                                            "(the stream runs on across steps, from an emptied cache "
+                                            "at frame 0)",
                                     "includes": "fused QKV projection + RoPE + append, residual"})
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle chain on a sample")
