@@ -43,52 +43,59 @@ __device__ inline void tile_ref(const AttnArgs& a, int s, int h, int t, int n_pa
 // w_i = exp(lse_i - max lse); lse = max + log(sum w).  Split i's partial
 // output arrives as fp16 words scaled by a power of two and the fp32 factor
 // f_i that undoes it (O_i = f_i * words), beside its LSE.  One thread per
-// (stream, head, query, 4 channels).
+// (stream, head, query, 8 channels): 16-byte loads of the words, and both
+// split loops unrolled so that their loads are in flight together (the merge
+// is latency-bound otherwise: a few bytes per thread per split).
 template <typename T>
 __global__ __launch_bounds__(256) void k_attend_combine(AttnArgs a) {
     const size_t idx = blockIdx.x * (size_t)256 + threadIdx.x;
-    const size_t total = (size_t)a.S * a.H * a.N * 16;
+    const size_t total = (size_t)a.S * a.H * a.N * 8;
     if (idx >= total) return;
-    const int d4 = idx & 15;
-    const size_t rest = idx >> 4;
+    const int d8 = idx & 7;
+    const size_t rest = idx >> 3;
     const int q = rest % a.N;
     const int sh = rest / a.N;   // s*H + h
     const int s = sh / a.H, h = sh % a.H;
     if (q >= a.states[s].n_query) return;   // not a token of this frame
     const size_t base = (size_t)sh * a.splits * a.N + q;
     float mx = -INFINITY;
+#pragma unroll 8
     for (int i = 0; i < a.splits; ++i) mx = fmaxf(mx, a.part_ls[base + (size_t)i * a.N].x);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f}, wsum = 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, wsum = 0.f;
     if (mx > -INFINITY) {
+#pragma unroll 4
         for (int i = 0; i < a.splits; ++i) {
             const size_t row = base + (size_t)i * a.N;
             const float2 ls = a.part_ls[row];
+            const uint4 u = *(const uint4*)(a.part_o + row * kHeadDim + d8 * 8);   // 8 fp16
             const float w = __expf(ls.x - mx);
             const float wf = w * ls.y;
-            const uint2 u = *(const uint2*)(a.part_o + row * kHeadDim + d4 * 4);   // 4 fp16
-            acc[0] += wf * (float)__builtin_bit_cast(_Float16, (uint16_t)(u.x & 0xFFFFu));
-            acc[1] += wf * (float)__builtin_bit_cast(_Float16, (uint16_t)(u.x >> 16));
-            acc[2] += wf * (float)__builtin_bit_cast(_Float16, (uint16_t)(u.y & 0xFFFFu));
-            acc[3] += wf * (float)__builtin_bit_cast(_Float16, (uint16_t)(u.y >> 16));
+            const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += wf * (float)__builtin_bit_cast(_Float16, (uint16_t)(uw[e] & 0xFFFFu));
+                acc[2 * e + 1] += wf * (float)__builtin_bit_cast(_Float16, (uint16_t)(uw[e] >> 16));
+            }
             wsum += w;
         }
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    T* op = (T*)a.out + (((size_t)s * a.N + q) * a.H + h) * kHeadDim + d4 * 4;
+    T* op = (T*)a.out + (((size_t)s * a.N + q) * a.H + h) * kHeadDim + d8 * 8;
     if constexpr (sizeof(T) == 2) {
-        uint32_t w[2];
+        uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
+        for (int e = 0; e < 4; ++e) {
             const __bf16 lo = (__bf16)(acc[2 * e] * inv);
             const __bf16 hi = (__bf16)(acc[2 * e + 1] * inv);
             w[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
                    ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
         }
-        *(uint2*)op = make_uint2(w[0], w[1]);
+        *(uint4*)op = make_uint4(w[0], w[1], w[2], w[3]);
     } else {
         *(float4*)op = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+        *(float4*)(op + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
     }
-    if (d4 == 0 && a.lse) a.lse[(size_t)sh * a.N + q] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
+    if (d8 == 0 && a.lse) a.lse[(size_t)sh * a.N + q] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
 }
 
 // fp32: one query per thread, fp32 throughout (precise exp/log).
@@ -170,7 +177,7 @@ hipError_t launch_attend(const AttnArgs& a, int dtype, hipStream_t st) {
     }
     hipError_t e = launch_attend_bf16_main(a, st);
     if (e != hipSuccess || a.splits == 1) return e;
-    const size_t total = (size_t)a.S * a.H * a.N * 16;
+    const size_t total = (size_t)a.S * a.H * a.N * 8;
     hipLaunchKernelGGL(k_attend_combine<uint16_t>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
                        st, a);
     return hipGetLastError();
