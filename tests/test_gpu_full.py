@@ -170,6 +170,26 @@ def test_large_grid_64x64():
     print(f"64x64 grid: max|out-oracle| {worst[0]:.3e}  max|lse-oracle| {worst[1]:.3e}")
 
 
+def test_large_grid_64x64_all_rows_at_recycle_and_last_frame():
+    """The 64x64 stream in full on two frames: every query row (6 specials and
+    4096 patches) of every head at the first recycled page (frame 21: 4
+    scale pages, the window of 16 after its first eviction, the frame's own
+    page) and the last frame (31), against the float64 oracle."""
+    wl = WORKLOADS[3]
+    cache = make_cache(wl)
+    run = Runner(wl, cache)
+    ost = OracleStream(wl, lambda f, t: qkv(wl, 0, 0, f, t))
+    worst = [0.0, 0.0]
+    for f, q, k, v in stream_frames(wl, None, chunk=16):
+        run.frame(f, q, k, v, wl.is_keyframe(f))
+        if f in (21, 31):
+            e, l = compare(run, ost, wl, f, rows=np.arange(wl.tokens))
+            worst = [max(worst[0], e), max(worst[1], l)]
+            print(f"64x64 frame {f}, all rows: max|out-oracle| {e:.3e}  max|lse-oracle| {l:.3e}", flush=True)
+    st = cache.state(0, 0)
+    assert st["fresh"] == wl.scale_frames + wl.sliding_window + 1, st["fresh"]
+
+
 def test_full_depth_cache_geometry_four_streams():
     """The cached layers of the full-depth stack at full geometry (4 streams,
     sf 8, window 32, keyframe every 2nd frame), fed seeded Q/K/V: two cached
