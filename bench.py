@@ -75,11 +75,12 @@ def source_digest(paths):
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload):
-    """HBM bytes per attend_frame call measured with rocprofv3 counters
-    (profiles/attend_hbm_traffic.json), if they were taken on the current
-    kernel sources for this workload; else None."""
-    p = os.path.join(ROOT, "profiles", "attend_hbm_traffic.json")
+def read_traffic(workload, record="attend_hbm_traffic.json"):
+    """HBM bytes per call of a kernel measured with rocprofv3 counters (a
+    record under profiles/: attend_hbm_traffic.json for attend_frame,
+    append_hbm_traffic.json for kv_append_frame), if they were taken on the
+    current kernel sources for this workload; else None."""
+    p = os.path.join(ROOT, "profiles", record)
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
@@ -438,7 +439,8 @@ def bench_append(wl, args, dev):
                        "grid": f"{wl.grid_h}x{wl.grid_w}", "heads": wl.heads,
                        "launches_per_step": wl.frames, "inputs": "cold (16 frames in rotation)"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": read_traffic(wl.name, "append_hbm_traffic.json"),
                          "avg_launch_us": round(us, 2), "algorithmic_bytes_per_launch": nbytes},
             "extra": extra}
 
