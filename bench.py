@@ -47,19 +47,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def visible_tokens(wl, f, interval=None, sf=None, w=None):
+def visible_tokens(wl, f, interval=None, sf=None, w=None, patches=None):
     """|T(f)|: retained tokens frame f attends to (keyframe schedule, scale
-    frames, window; own frame always visible)."""
+    frames, window; own frame always visible); patches: tokens per patch page
+    when every frame has a grid of its own."""
     iv = wl.keyframe_interval if interval is None else interval
     sf = wl.scale_frames if sf is None else sf
     w = wl.sliding_window if w is None else w
     m = (f + iv - 1) // iv if iv > 0 else 0                   # keyframes before f
     n_patch_frames = min(m, sf) + min(max(m - sf, 0), w) + 1
-    return n_patch_frames * wl.patches + (m + 1) * wl.n_special
+    return n_patch_frames * (wl.patches if patches is None else patches) + (m + 1) * wl.n_special
 
 
-def attn_flops(wl, f, **kw):
-    return 4.0 * wl.heads * wl.head_dim * wl.tokens * visible_tokens(wl, f, **kw) * wl.streams
+def attn_flops(wl, f, queries=None, **kw):
+    n_q = wl.tokens if queries is None else queries
+    return 4.0 * wl.heads * wl.head_dim * n_q * visible_tokens(wl, f, **kw) * wl.streams
 
 
 def append_bytes(wl):
@@ -215,11 +217,17 @@ def bench_single_layer(wl, args, dev):
     lse = torch.empty((wl.streams, wl.heads, wl.tokens), dtype=torch.float32, device=dev)
     keyf = [int(wl.is_keyframe(f)) for f in range(wl.frames)]
     F = wl.frames
+    grid, npatch = None, wl.patches
+    if args.grid:   # every frame of its own (smaller) grid inside the configured pages
+        gh, gw = (int(v) for v in args.grid.lower().split("x"))
+        if not (1 <= gh <= wl.grid_h and 1 <= gw <= wl.grid_w):
+            raise SystemExit(f"--grid {args.grid}: at most {wl.grid_h}x{wl.grid_w}")
+        grid, npatch = (gh, gw), gh * gw
 
     def one_pass(ev=None):
         cache.reset(0)
         for f in range(F):
-            cache.append(0, f, keyf[f], q_all[f], k_all[f], v_all[f], q_rot)
+            cache.append(0, f, keyf[f], q_all[f], k_all[f], v_all[f], q_rot, grid=grid)
             if ev is not None:
                 ev[f][0].record()
             cache.attend(0, q_rot, out, lse)
@@ -239,15 +247,17 @@ def bench_single_layer(wl, args, dev):
     elapsed = time.perf_counter() - t0
 
     att_ms = np.array([[e[f][0].elapsed_time(e[f][1]) for f in range(F)] for e in events])
-    flops = np.array([attn_flops(wl, f) for f in range(F)])
+    flops = np.array([attn_flops(wl, f, queries=wl.n_special + npatch, patches=npatch)
+                      for f in range(F)])
     steady = [f for f in range(F) if f >= wl.scale_frames + wl.sliding_window]
     extra = {}
     if steady:
         extra["attend_tflops_steady"] = round(
             float(flops[steady].mean() / (att_ms[:, steady].mean() / 1e3) / 1e12), 2)
     res = result_line(wl, args, elapsed, F * wl.streams, att_ms, np.tile(flops, (args.steps, 1)),
-                      cache.info()["attn_splits"], extra=extra)
-    if not args.no_cpu_baseline:
+                      cache.info()["attn_splits"], extra=extra,
+                      config_extra={"frame_grid": args.grid} if grid else None)
+    if not args.no_cpu_baseline and grid is None:
         log("[bench] timing the CPU oracle on a sample")
         res["cpu_baseline"] = cpu_baseline(wl)
     return res
@@ -371,6 +381,7 @@ def bench_append(wl, args, dev):
     than the caches hold at four streams) and warm (one frame's inputs, read
     by the previous call: what a producer that has just written q, k, v
     gives)."""
+    import dataclasses
     import time
 
     import torch
@@ -378,6 +389,18 @@ def bench_append(wl, args, dev):
     import rope_paged_kv_amd as rp
     from rpkv_inputs import frame_qkv
 
+    if args.rope_layout == "half_split":
+        # the 2D module's form: half-split axis blocks, pairs (0, 16, 16), base 100
+        wl = dataclasses.replace(wl, name=wl.name + "_halfsplit", pairs=(0, 16, 16), theta=100.0,
+                                 rope_layout=1)
+    grid = None
+    ntok = wl.tokens
+    if args.grid:
+        gh, gw = (int(v) for v in args.grid.lower().split("x"))
+        if not (1 <= gh <= wl.grid_h and 1 <= gw <= wl.grid_w):
+            raise SystemExit(f"--grid {args.grid}: at most {wl.grid_h}x{wl.grid_w}")
+        grid = (gh, gw)
+        ntok = wl.n_special + gh * gw
     nf = 16
     qkv = [tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in frame_qkv(wl, 0, f))
            for f in range(nf)]
@@ -390,8 +413,9 @@ def bench_append(wl, args, dev):
                          max_keyframes=wl.n_keyframes(), rope=spec)
     cache = rp.PagedKVCache(cfg, device=dev)
     q_rot = torch.empty_like(qkv[0][0])
-    nbytes = append_bytes(wl)
-    src = [torch.cat([t.reshape(-1) for t in f]) for f in qkv]   # the same bytes as q, k, v
+    # bytes of the tokens a call reads and writes (a frame of its own grid: only those)
+    nbytes = append_bytes(wl) * ntok / wl.tokens
+    src = [torch.cat([t[:, :ntok].reshape(-1) for t in f]) for f in qkv]   # the same bytes as q, k, v
     dst = torch.empty_like(src[0])
     assert 2 * src[0].numel() * src[0].element_size() == nbytes
 
@@ -400,12 +424,12 @@ def bench_append(wl, args, dev):
     cache.reset(0)
     for f in range(f_pos):
         q, k, v = qkv[f % nf]
-        cache.append(0, f, int(wl.is_keyframe(f)), q, k, v, q_rot)
+        cache.append(0, f, int(wl.is_keyframe(f)), q, k, v, q_rot, grid=grid)
         cache.evict(0)
     commit = int(wl.is_keyframe(f_pos))
 
     def append_fn(rot):
-        return lambda i: cache.append(0, f_pos, commit, *qkv[i % nf if rot else 0], q_rot)
+        return lambda i: cache.append(0, f_pos, commit, *qkv[i % nf if rot else 0], q_rot, grid=grid)
 
     def copy_fn(rot):
         return lambda i: dst.copy_(src[i % nf if rot else 0])
@@ -437,7 +461,9 @@ def bench_append(wl, args, dev):
             "higher_is_better": True, "dtype": wl.dtype, "data": "synthetic",
             "config": {"workload": wl.name, "streams": wl.streams,
                        "grid": f"{wl.grid_h}x{wl.grid_w}", "heads": wl.heads,
-                       "launches_per_step": wl.frames, "inputs": "cold (16 frames in rotation)"},
+                       "launches_per_step": wl.frames, "inputs": "cold (16 frames in rotation)",
+                       "rope_layout": "half_split" if wl.rope_layout == 1 else "interleaved",
+                       "frame_grid": f"{grid[0]}x{grid[1]}" if grid else f"{wl.grid_h}x{wl.grid_w}"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": read_traffic(wl.name, "append_hbm_traffic.json"),
@@ -453,6 +479,12 @@ def main():
     ap.add_argument("--workload", type=int, default=4, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--append-only", action="store_true",
                     help="time kv_append_frame alone at the workload's geometry")
+    ap.add_argument("--rope-layout", choices=["interleaved", "half_split"], default="interleaved",
+                    help="--append-only: rotary layout (half_split: the 2D module's half-split "
+                         "axis blocks, pairs 0/16/16, base 100)")
+    ap.add_argument("--grid", default=None,
+                    help="single-layer workloads and --append-only: every frame of its own patch "
+                         "grid HxW inside the workload's pages (kv_append_frame_grid)")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,

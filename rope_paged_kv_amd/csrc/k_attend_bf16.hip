@@ -96,26 +96,33 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_over(const char* p, size_t bytes
 // A walk over the key tiles of one split, one tile at a time (all scalar):
 // patch tiles page by page through the visible table (the page id read once
 // per page), then the special stream's tiles.  The number of patch tiles npt
-// and tiles per page tpp are the split's (passed in, not stored).
+// and tiles per whole page tpp are the split's (passed in, not stored).  When
+// some visible page holds fewer tokens than a whole grid, tpre (the running
+// key-tile counts of the visible pages, else null) gives each page its own
+// ceil(len / 64) tiles, so no tile past a page's tokens is walked.
 // (readfirstlane keeps every field in scalar registers: the integer
 // division would otherwise come back in a vector register, and the page id
 // with it, turning each tile load into a loop over lanes.)
 struct TileWalk {
-    int t, pi, tip, page;
-    __device__ void init(int t0, int npt, int tpp, cint_ptr vis) {
+    int t, pi, tip, page, ntp;   // ntp: tiles of page pi
+    __device__ void init(int t0, int npt, int tpp, cint_ptr vis, cint_ptr tpre) {
         t = uniform(t0);
-        pi = uniform(t / tpp);
-        tip = uniform(t - pi * tpp);
+        pi = uniform(t / tpp);   // a page holds at most tpp tiles: at or before t's page
+        if (tpre && t < npt)
+            while (t >= uniform(tpre[pi + 1])) pi = uniform(pi + 1);
+        tip = uniform(tpre ? t - (t < npt ? uniform(tpre[pi]) : 0) : t - pi * tpp);
+        ntp = tpre && t < npt ? uniform(tpre[pi + 1] - tpre[pi]) : tpp;
         page = t < npt ? uniform(vis[pi]) : 0;
     }
     // returns true when the walk enters a new patch page
-    __device__ bool next(int npt, int tpp, cint_ptr vis) {
+    __device__ bool next(int npt, int tpp, cint_ptr vis, cint_ptr tpre) {
         ++t;
-        if (++tip == tpp) {
+        if (++tip == ntp) {
             tip = 0;
             ++pi;
             if (t < npt) {
                 page = uniform(vis[pi]);
+                if (tpre) ntp = uniform(tpre[pi + 1] - tpre[pi]);
                 return true;
             }
         }
@@ -358,7 +365,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         ld.lvs0 = lvs[0];
         ld.lvs1 = lvs[1];
     }
-    const int n_patch_tiles = vis_n * a.tpp;
+    // Pages that hold fewer tokens than a whole grid: walk their own tiles
+    // only (running counts written with the visible table).
+    const bool vis_full = uniform(st->vis_full) != 0;
+    const cint_ptr tpre = vis_full ? nullptr : (cint_ptr)(uintptr_t)st->vis_tpre;
+    const int n_patch_tiles = vis_full ? vis_n * a.tpp : uniform(tpre[vis_n]);
     const int n_tiles = n_patch_tiles + (vis_sp + kTile - 1) / kTile;
     const int t0 = uniform((int)((long long)split * n_tiles / a.splits));
     const int t1 = uniform((int)((long long)(split + 1) * n_tiles / a.splits));
@@ -409,7 +420,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
     // Page lengths: all P when every visible page holds a whole grid (then
     // nothing is read per tile), else an LDS copy.
-    const bool vis_full = uniform(st->vis_full) != 0;
     if (!vis_full)
         for (int i = tid; i < vis_n; i += 256) s_vlen[i] = st->vis_len[i];
     auto page_len = [&](int pi) { return vis_full ? a.P : uniform(s_vlen[pi]); };
@@ -422,27 +432,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         // holds the tokens its frame had, the special stream vis_sp).
         const int npt = n_patch_tiles, tpp = a.tpp;
         TileWalk wk, wv;
-        wk.init(t0, npt, tpp, ld.vis);
+        wk.init(t0, npt, tpp, ld.vis, tpre);
         wv = wk;
         int plen = wv.t < npt ? page_len(wv.pi) : 0;   // tokens of wv's page
         auto tile_len = [&]() {
             return wv.t < npt ? min(kTile, plen - wv.tip * kTile) : min(kTile, vis_sp - (wv.t - npt) * kTile);
         };
         auto next_v = [&]() {
-            if (wv.next(npt, tpp, ld.vis)) plen = page_len(wv.pi);
+            if (wv.next(npt, tpp, ld.vis, tpre)) plen = page_len(wv.pi);
         };
         // Prologue: K(0..2) and V^T(0..1); the V^T stage the first step's
         // (empty) products read is zeroed so that stale LDS contents cannot
         // reach them.
         ld.issue_k(wk, npt, k0, wave);
-        wk.next(npt, tpp, ld.vis);
+        wk.next(npt, tpp, ld.vis, tpre);
         if (n > 1) {
             ld.issue_k(wk, npt, k1, wave);
-            wk.next(npt, tpp, ld.vis);
+            wk.next(npt, tpp, ld.vis, tpre);
         }
         if (n > 2) {
             ld.issue_k(wk, npt, k2, wave);
-            wk.next(npt, tpp, ld.vis);
+            wk.next(npt, tpp, ld.vis, tpre);
         }
         int la = 0, lb = 0, lc = 0;   // valid keys of tiles i, i+1, i+2 (rotating)
         ld.issue_v(wv, npt, v0, wave);
@@ -495,7 +505,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             int issued = 0;   // loads of this wave in flight from this barrier
             if (i + 3 < n) {
                 ld.issue_k(wk, npt, kc, wave);
-                wk.next(npt, tpp, ld.vis);
+                wk.next(npt, tpp, ld.vis, tpre);
                 issued += 2;
             }
             if (i + 2 < n) {

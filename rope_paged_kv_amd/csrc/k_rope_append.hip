@@ -22,7 +22,9 @@
 // Layout of the work: one workgroup per (tile of 64 tokens, head, stream);
 // tile 0 carries the special tokens.  Each thread moves 16-byte chunks, so
 // every row (one token of one head, 128 B in bf16) is read and written with
-// full-width coalesced accesses; V goes through LDS to be written transposed
+// full-width coalesced accesses (in the half-split layout a chunk's rotation
+// partner is read from the lane that loaded it); V goes through LDS to be
+// written transposed
 // (the layout the attention kernel's matrix-core operands read).  The
 // bookkeeping never leaves the device: every workgroup derives the target page
 // from the state as it stands (which no workgroup of the launch modifies), and
@@ -71,17 +73,19 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         int r, c;
-        chunk_of<CH, LAYOUT>(a, tid, i, r, c);
+        chunk_of<CH>(tid, i, r, c);
         const size_t off = (size_t)(r < nrows ? r : 0) * rs + c * CH;
         qv[i] = *(const uint4*)(qb + off);
         kv[i] = *(const uint4*)(kb + off);
         vv[i] = *(const uint4*)(vb + off);
     }
-    float2 cs[PER * CH / 2];
+    // interleaved: pair e of slot i at [i*CH/2 + e]; half-split: the pair
+    // of channel e of slot i at [i*CH + e]
+    float2 cs[LAYOUT == RPKV_ROPE_INTERLEAVED ? PER * CH / 2 : PER * CH];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         int r, c;
-        chunk_of<CH, LAYOUT>(a, tid, i, r, c);
+        chunk_of<CH>(tid, i, r, c);
         int hp = 0, wp = 0;   // specials sit at h = w = 0
         if (!special) {
             const int p = r < nrows ? slot0 + r : 0;   // rows past the frame's patches: (0, 0)
@@ -91,9 +95,12 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
         if (LAYOUT == RPKV_ROPE_INTERLEAVED) {
 #pragma unroll
             for (int e = 0; e < CH / 2; ++e) cs[i * (CH / 2) + e] = coeff_of<CH, LAYOUT>(a, c, e, hp, wp);
-        } else if ((i & 1) == 0) {
+        } else {
+            bool first;
+            int dc, cf;
+            half_partner<CH>(a, c, first, dc, cf);
 #pragma unroll
-            for (int e = 0; e < CH; ++e) cs[(i >> 1) * CH + e] = coeff_of<CH, LAYOUT>(a, c, e, hp, wp);
+            for (int e = 0; e < CH; ++e) cs[i * CH + e] = coeff_of<CH, LAYOUT>(a, cf, e, hp, wp);
         }
     }
 
@@ -129,23 +136,39 @@ __global__ __launch_bounds__(256) void k_rope_append(AppendArgs a) {
                 fk[i][2 * e + 1] = xk * w.y + yk * w.x;
             }
     } else {
+        // The pair partner of a lane's chunk sits in the same row, so in the
+        // same wave, dc lanes away: read across lanes, then each lane rotates
+        // its own chunk (first half: x cos - y sin; second half: x cos + y sin,
+        // x its own value and y the partner's).
+        const int lane = tid & 63;
 #pragma unroll
-        for (int j = 0; j < PER / 2; ++j)
+        for (int i = 0; i < PER; ++i) {
+            int r, c;
+            chunk_of<CH>(tid, i, r, c);
+            bool first;
+            int dc, cf;
+            half_partner<CH>(a, c, first, dc, cf);
+            const int pl = lane + dc;
+            const uint4 pq = make_uint4(__shfl((int)qv[i].x, pl), __shfl((int)qv[i].y, pl),
+                                        __shfl((int)qv[i].z, pl), __shfl((int)qv[i].w, pl));
+            const uint4 pk = make_uint4(__shfl((int)kv[i].x, pl), __shfl((int)kv[i].y, pl),
+                                        __shfl((int)kv[i].z, pl), __shfl((int)kv[i].w, pl));
+            float gq[CH], gk[CH];
+            Vec<T>::unpack(pq, gq);
+            Vec<T>::unpack(pk, gk);
 #pragma unroll
             for (int e = 0; e < CH; ++e) {
-                const float2 w = cs[j * CH + e];
-                const float xq = fq[2 * j][e], yq = fq[2 * j + 1][e];
-                fq[2 * j][e] = xq * w.x - yq * w.y;
-                fq[2 * j + 1][e] = yq * w.x + xq * w.y;
-                const float xk = fk[2 * j][e], yk = fk[2 * j + 1][e];
-                fk[2 * j][e] = xk * w.x - yk * w.y;
-                fk[2 * j + 1][e] = yk * w.x + xk * w.y;
+                const float2 w = cs[i * CH + e];
+                const float xq = fq[i][e], yq = gq[e], xk = fk[i][e], yk = gk[e];
+                fq[i][e] = first ? xq * w.x - yq * w.y : xq * w.x + yq * w.y;
+                fk[i][e] = first ? xk * w.x - yk * w.y : xk * w.x + yk * w.y;
             }
+        }
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         int r, c;
-        chunk_of<CH, LAYOUT>(a, tid, i, r, c);
+        chunk_of<CH>(tid, i, r, c);
         const bool valid = r < nrows;
         if (valid) {
             *(uint4*)(qrb + r * rs + c * CH) = Vec<T>::pack(fq[i]);

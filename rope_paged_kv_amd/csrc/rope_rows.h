@@ -93,27 +93,42 @@ __device__ inline int pair_chunk(const AppendArgs& a, int pc, int second) {
     return base + pc + (second ? half : 0);
 }
 
-// Row and 16-byte chunk of a thread's chunk slot i.  Interleaved layout:
-// slots walk the tile's chunks in order.  Half-split layout: slots 2j and
-// 2j+1 are a pair of chunks that rotate together -- a chunk of the first half
-// of an axis block and the chunk pairs_a channels after it -- and the pair
-// slots walk the tile's first-half chunks in order (cpr/2 per row).
-template <int CH, int LAYOUT>
-__device__ inline void chunk_of(const AppendArgs& a, int tid, int i, int& r, int& c) {
+// Row and 16-byte chunk of a thread's chunk slot i (256 threads): the slots
+// walk the tile's chunks in order, so the lanes of a wave cover whole rows
+// and every access is a full-width coalesced row.
+template <int CH>
+__device__ inline void chunk_of(int tid, int i, int& r, int& c) {
     constexpr int CPR = kHeadDim / CH;
-    if (LAYOUT == RPKV_ROPE_INTERLEAVED) {
-        const int id = tid + i * 256;
-        r = id / CPR;
-        c = id % CPR;
-        return;
+    const int id = tid + i * 256;
+    r = id / CPR;
+    c = id % CPR;
+}
+
+// Half-split layout: the rotation partner of chunk c of a row -- dc chunks
+// away, the chunk pairs_a channels after c in its axis block (c in the first
+// half) or before it -- and the first-half chunk of the pair, which names the
+// pair's coefficients.
+template <int CH>
+__device__ inline void half_partner(const AppendArgs& a, int c, bool& first, int& dc, int& cfirst) {
+    const int nt = a.pt / CH, nh = a.ph / CH, nw = a.pw / CH;   // first-half chunks per axis
+    int base, half;
+    if (c < 2 * nt) {
+        base = 0;
+        half = nt;
+    } else if (c < 2 * (nt + nh)) {
+        base = 2 * nt;
+        half = nh;
+    } else {
+        base = 2 * (nt + nh);
+        half = nw;
     }
-    const int id = tid + (i >> 1) * 256;
-    r = id / (CPR / 2);
-    c = pair_chunk<CH>(a, id % (CPR / 2), i & 1);
+    first = c - base < half;
+    dc = first ? half : -half;
+    cfirst = first ? c : c - half;
 }
 
 // Rotation coefficients of a thread's chunk slots, flat: interleaved, pair e
-// of slot i at [i*CH/2 + e]; half-split, channel e of pair slot j at [j*CH + e].
+// of slot i; half-split, the pair of channel e of first-half chunk c.
 template <int CH, int LAYOUT>
 __device__ inline float2 coeff_of(const AppendArgs& a, int c, int e, int hp, int wp) {
     if (LAYOUT == RPKV_ROPE_INTERLEAVED) return coeff(a, c * (CH / 2) + e, hp, wp);
@@ -156,14 +171,37 @@ __device__ inline void write_frame_record(const AppendArgs& a, CacheState* st, c
     // own page (it comes last whether it will be committed or not).
     const int ns = st->n_scale, nw = st->n_win, head = st->win_head;
     const int vis_n = tg.ok ? ns + nw + 1 : 0;
-    int full = 1;
-    for (int i = tid; i < vis_n; i += 256) {
-        const int pg = i < ns ? st->scale[i] : (i < ns + nw ? st->win[(head + i - ns) % kMaxPool] : tg.page);
-        st->vis[i] = pg;
-        const int len = i < ns + nw ? st->page_tokens[pg] : a.fP;
-        st->vis_len[i] = len;
-        full &= len == a.P;
+    // Thread tid takes pages 2 tid and 2 tid + 1 (at most kMaxPool = 512), then
+    // the workgroup scans their key-tile counts (ceil(len / kTile)) into the
+    // running counts the attention walks a split's tiles by.
+    __shared__ int tiles_scan[256];
+    int full = 1, own = 0, first_tiles = 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int i = 2 * tid + k;
+        if (i < vis_n) {
+            const int pg = i < ns ? st->scale[i] : (i < ns + nw ? st->win[(head + i - ns) % kMaxPool] : tg.page);
+            st->vis[i] = pg;
+            const int len = i < ns + nw ? st->page_tokens[pg] : a.fP;
+            st->vis_len[i] = len;
+            full &= len == a.P;
+            const int nt = (len + kTile - 1) / kTile;
+            if (k == 0) first_tiles = nt;
+            own += nt;
+        }
     }
+    tiles_scan[tid] = own;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {   // inclusive scan (Hillis-Steele)
+        const int v = tid >= off ? tiles_scan[tid - off] : 0;
+        __syncthreads();
+        tiles_scan[tid] += v;
+        __syncthreads();
+    }
+    const int before = tiles_scan[tid] - own;   // tiles of pages 0 .. 2 tid - 1
+    if (2 * tid <= vis_n) st->vis_tpre[2 * tid] = before;
+    if (2 * tid + 1 <= vis_n) st->vis_tpre[2 * tid + 1] = before + first_tiles;
+    if (tid == 255) st->vis_tpre[vis_n] = tiles_scan[255];   // the total (also for vis_n = 512)
     full = __syncthreads_and(full);
     if (tid == 0) {
         st->n_query = a.nsp + a.fP;

@@ -39,6 +39,10 @@ struct CacheState {
     int vis[kMaxPool];  // visible patch pages in attention order
     int vis_len[kMaxPool];      // tokens of each visible patch page
     int page_tokens[kMaxPool];  // tokens stored in each pool page (its frame's patches)
+    // key tiles of the visible patch pages before page i (ceil(len / kTile)
+    // each); [vis_n] is their total.  Written with the visible table, read
+    // when vis_full is 0.
+    int vis_tpre[kMaxPool + 1];
 };
 
 // Storage position <-> key index inside an aligned group of 16 slots of a
