@@ -359,13 +359,15 @@ def test_single_layer_37x37_all_rows_at_transitions():
     print(f"37x37 all rows at frames 24, 25, 63: max|out-oracle| {worst:.3e}  max|lse-oracle| {worst_lse:.3e}")
 
 
-def test_variable_patch_grids():
+@pytest.mark.parametrize("splits", [0, 3, 7])
+def test_variable_patch_grids(splits):
     """Frames of their own grids (9x11, 7x11, 5x6, 1x1, 9x7 in a 9x11 page):
     pages record their token counts, q_rot and K follow each frame's grid,
     attention reads the valid tokens of every page and answers the frame's
-    own tokens only (the rows past them keep what they held)."""
+    own tokens only (the rows past them keep what they held).  Pages of one
+    and of two key tiles mix, so splits start inside pages of either kind."""
     wl = small_variants()["small_vargrid"]
-    cache = make_cache(wl)
+    cache = make_cache(wl, splits=splits)
     run = Runner(wl, cache)
     sim = sim_for(wl)
     orc = OracleStream(wl, lambda f, t: qkv(wl, 0, 0, f, t))
@@ -397,6 +399,28 @@ def test_variable_patch_grids():
         assert torch.all(run.out[0, n:] == 7.0) and torch.all(run.lse[0, :, n:] == 7.0), f
         sim.evict()
         cache.evict(0)
+
+
+@pytest.mark.parametrize("splits", [0, 5])
+def test_variable_grids_37x37_through_eviction(splits):
+    """37x37 pages holding frames of five grids (whole, 33x33, 20x30, 37x36,
+    1x1: 22, 18, 10, 21 and 1 key tiles) through the first eviction (frame
+    24) and recycled pages: the attention walks each page's own tiles and
+    the splits cut across pages of different lengths.  Sampled rows of each
+    frame's own tokens (specials, first and last patch, 40 others) against
+    the float64 oracle."""
+    wl = WORKLOADS[1].replace(name="vargrid_37x37", frames=30,
+                              grids=((37, 37), (33, 33), (20, 30), (37, 36), (1, 1)))
+
+    def rows(f):
+        n = wl.frame_tokens(f)
+        rng = np.random.default_rng(f)
+        inner = np.arange(wl.n_special + 1, max(n - 1, wl.n_special + 1))
+        pr = rng.choice(inner, min(40, len(inner)), replace=False) if len(inner) else []
+        return np.unique(np.r_[np.arange(min(n, wl.n_special + 1)), n - 1, pr].astype(int))
+
+    worst, worst_lse = run_and_compare(wl, {3, 4, 9, 23, 24, 25, 29}, rows=rows, splits=splits)
+    print(f"variable grids 37x37, splits {splits}: max|out-oracle| {worst:.3e}  max|lse-oracle| {worst_lse:.3e}")
 
 
 def test_append_grid_is_checked():
