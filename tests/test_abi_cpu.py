@@ -91,3 +91,13 @@ def test_residual_add_validates_before_launching():
             r.residual_add_bf16(x, o, xb, n, 0)
         assert e.value.code == r.RPKV_EINVAL, (x, o, xb, n)
     r.residual_add_bf16(256, 512, None, 0, 0)   # n = 0 launches nothing
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """No fallback: without librpkv.so the binding raises instead of running
+    anything else."""
+    from rope_paged_kv_amd import _abi
+    monkeypatch.setattr(_abi, "_lib", None)
+    monkeypatch.setattr(_abi, "LIB_PATH", "/nonexistent/librpkv.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        _abi.load()
