@@ -194,7 +194,8 @@ def test_full_depth_cache_geometry_four_streams():
     """The cached layers of the full-depth stack at full geometry (4 streams,
     sf 8, window 32, keyframe every 2nd frame), fed seeded Q/K/V: two cached
     layers of one handle, checked on two streams at the eviction and recycle
-    transitions; plus a frame (no-cache) layer on the same frames."""
+    transitions (every row of one stream and layer at the first recycled page,
+    frame 82); plus a frame (no-cache) layer on the same frames."""
     wl = WORKLOADS[4]
     layers = (3, 17)                       # input keys of handle layers 0 and 1
     cache = make_cache(wl, layers=2)
@@ -213,7 +214,10 @@ def test_full_depth_cache_geometry_four_streams():
             run.frame(f, torch.roll(q, sh, 2), torch.roll(k, sh, 2), torch.roll(v, sh, 2), kf)
             if f in check:
                 for s in (0, 3):
-                    compare(run, orc[(i, s)], wl, f, s=s, rows=sampled_rows(wl, f, 12))
+                    # the first recycled page (frame 82): every row of stream 0, layer 0
+                    full = f == 82 and i == 0 and s == 0
+                    compare(run, orc[(i, s)], wl, f, s=s,
+                            rows=np.arange(wl.tokens) if full else sampled_rows(wl, f, 12))
         frun.frame(f, q, k, v, False, evict=False)
         if f in check:
             compare(frun, forc, fwl, f, s=1, rows=sampled_rows(wl, f, 12))
