@@ -501,6 +501,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": n, "copies": 3}))
         return
+    if args.rope_layout != "interleaved" and not args.append_only:
+        raise SystemExit("--rope-layout applies to --append-only (the other lines run the workload's layout)")
+    if args.grid and not args.append_only and args.workload == 4:
+        raise SystemExit("--grid applies to the single-layer workloads and to --append-only")
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               f"(streams and heads shard without communication: run one process per GPU)",
